@@ -1,0 +1,152 @@
+"""Seeded synthetic inputs for the fp8 block-scaled GEMM, shared by the tests, the bench
+and the smoke check.
+
+This module generates and quantises operands; it holds none of the GEMM's arithmetic and
+is imported by both the oracle side and the GPU side so that both consume the same bytes.
+
+Recipe (the workloads of page "Flydsl Fp8 Blockscale Gemm", "When to use" table, with
+synthetic values standing in for the model activations and weights measured there):
+
+* ``rng = numpy.random.default_rng(seed)``; ``A = rng.standard_normal((M, K), float32)``,
+  then ``B = 0.02 * rng.standard_normal((N, K), float32)``, drawn in that order.
+* Route BS: A is quantised per 1x128 group along K and B per 128x128 block, each with the
+  fp32 scale ``s = amax / 448`` (``s = 1`` when the group is all zero) and codes
+  ``e4m3_rne_saturate(x / s)``.
+* Route MX: A and B are quantised per 1x32 group along K with a ue8m0 exponent ``e``, the
+  smallest integer with ``amax <= 448 * 2^e`` (clamped to [-127, 127]; byte ``e + 127``;
+  byte 127 when the group is all zero), and codes ``e4m3_rne_saturate(x * 2^-e)``.
+
+The e4m3 encoder is torch's fp32 -> float8_e4m3fn conversion (round to nearest even) applied
+after clamping to +-448.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+E4M3_MAX = 448.0
+
+# The five workloads the bench and the parity tests use, as (M, N, K) and route.
+CONFIGS = {
+    "tiny": dict(M=128, N=256, K=512, route="bs"),
+    "narrow_n": dict(M=4096, N=2048, K=7168, route="bs"),
+    "k_light": dict(M=16384, N=7168, K=768, route="bs"),
+    "wide_n": dict(M=4096, N=65536, K=1536, route="bs"),
+    "mxfp8": dict(M=16384, N=8192, K=1280, route="mx"),
+}
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """fp32 -> OCP e4m3 codes (uint8), round to nearest even, saturating at +-448."""
+    t = torch.from_numpy(np.clip(np.asarray(x, dtype=np.float32), -E4M3_MAX, E4M3_MAX))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def draw(M: int, N: int, K: int, seed: int):
+    """The raw fp32 operands: A ~ N(0,1) [M,K], B ~ N(0,0.02^2) [N,K]."""
+    rng = np.random.default_rng(seed)
+    A = rng.standard_normal((M, K), dtype=np.float32)
+    B = (np.float32(0.02) * rng.standard_normal((N, K), dtype=np.float32)).astype(np.float32)
+    return A, B
+
+
+def quantize_groups_fp32(x: np.ndarray, rows: int, cols: int):
+    """Quantise x [R, C] in blocks of rows x cols with fp32 scale amax/448.
+
+    Returns (codes uint8 [R, C], scales fp32 [ceil(R/rows), C/cols])."""
+    R, C = x.shape
+    if C % cols:
+        raise ValueError("columns must divide into groups")
+    Rp = -(-R // rows) * rows
+    xp = x if Rp == R else np.concatenate([x, np.zeros((Rp - R, C), np.float32)])
+    blocks = xp.reshape(Rp // rows, rows, C // cols, cols)
+    amax = np.abs(blocks).max(axis=(1, 3)).astype(np.float32)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    scale[amax == 0] = np.float32(1.0)
+    q = blocks / scale[:, None, :, None]
+    codes = e4m3_encode(q.reshape(Rp, C).astype(np.float32))[:R]
+    return np.ascontiguousarray(codes), np.ascontiguousarray(scale)
+
+
+def e8m0_exponents(amax: np.ndarray) -> np.ndarray:
+    """Smallest integer e with amax <= 448 * 2^e (exact), clamped to [-127, 127];
+    0 for all-zero groups."""
+    amax = np.asarray(amax, dtype=np.float64)
+    safe = np.where(amax > 0, amax, 1.0)
+    e = np.ceil(np.log2(safe / E4M3_MAX)).astype(np.int64)
+    # Correct any off-by-one of the floating log2 with exact power-of-two comparisons.
+    e = np.where(safe > np.ldexp(E4M3_MAX, e), e + 1, e)
+    e = np.where(safe <= np.ldexp(E4M3_MAX, e - 1), e - 1, e)
+    e = np.where(amax > 0, e, 0)
+    return np.clip(e, -127, 127)
+
+
+def quantize_mx(x: np.ndarray, group: int = 32):
+    """Quantise x [R, C] per 1 x group with ue8m0 scales.
+
+    Returns (codes uint8 [R, C], e8m0 bytes uint8 [R, C/group])."""
+    R, C = x.shape
+    if C % group:
+        raise ValueError("columns must divide into groups")
+    g = x.reshape(R, C // group, group)
+    e = e8m0_exponents(np.abs(g).max(axis=2))
+    q = np.ldexp(g.astype(np.float64), -e[:, :, None]).astype(np.float32)  # exact scaling
+    codes = e4m3_encode(q.reshape(R, C))
+    return np.ascontiguousarray(codes), np.ascontiguousarray((e + 127).astype(np.uint8))
+
+
+@dataclass
+class BSInputs:
+    M: int
+    N: int
+    K: int
+    A: np.ndarray        # uint8 [M, K] e4m3 codes
+    a_scale: np.ndarray  # float32 [M, K/128]   logical a_s[m, kb]
+    B: np.ndarray        # uint8 [N, K] e4m3 codes
+    b_scale: np.ndarray  # float32 [N/128, K/128]
+
+    @property
+    def a_scale_kmajor(self) -> np.ndarray:
+        """a_scale laid out K-block-major, [K/128, M] contiguous (the library's layout)."""
+        return np.ascontiguousarray(self.a_scale.T)
+
+
+@dataclass
+class MXInputs:
+    M: int
+    N: int
+    K: int
+    A: np.ndarray        # uint8 [M, K]
+    a_e8m0: np.ndarray   # uint8 [M, K/32]
+    B: np.ndarray        # uint8 [N, K]
+    b_e8m0: np.ndarray   # uint8 [N, K/32]
+
+
+def bs_inputs(M: int, N: int, K: int, seed: int = 0) -> BSInputs:
+    """Route-BS operands: A per-1x128, B per-128x128, fp32 scales amax/448."""
+    A, B = draw(M, N, K, seed)
+    qa, sa = quantize_groups_fp32(A, 1, 128)
+    del A
+    qb, sb = quantize_groups_fp32(B, 128, 128)
+    return BSInputs(M, N, K, qa, sa, qb, sb)
+
+
+def mx_inputs(M: int, N: int, K: int, seed: int = 0) -> MXInputs:
+    """Route-MX operands: A and B per-1x32 with ue8m0 exponents."""
+    A, B = draw(M, N, K, seed)
+    qa, ea = quantize_mx(A)
+    del A
+    qb, eb = quantize_mx(B)
+    return MXInputs(M, N, K, qa, ea, qb, eb)
+
+
+def sample_indices(n_total: int, n_pick: int, seed: int) -> np.ndarray:
+    """A seeded, sorted sample of distinct indices that always includes the first and last."""
+    if n_pick >= n_total:
+        return np.arange(n_total, dtype=np.int32)
+    rng = np.random.default_rng(seed + 7919)
+    pick = rng.choice(n_total, size=n_pick, replace=False)
+    pick[0], pick[-1] = 0, n_total - 1
+    return np.unique(pick).astype(np.int32)

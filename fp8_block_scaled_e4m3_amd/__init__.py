@@ -1,0 +1,171 @@
+"""fp8_block_scaled_e4m3_amd -- thin Python binding of libfp8bs, the gfx950 fp8 block-scaled GEMM.
+
+Every function here only marshals arguments (torch tensors -> device pointers, the current
+torch stream -> hipStream_t) and calls the C ABI declared in ``include/fp8bs.h`` under the
+same name. All computation runs in the HIP library; there is no CPU or PyTorch fallback, and
+importing this package fails loudly when the library has not been built.
+
+Routes (see include/fp8bs.h for layouts and constraints):
+
+* ``fp8bs_gemm(A, a_scale, B_prep, b_scale, C)`` -- fp32 per-1x128 activation scales
+  (``a_scale`` laid out [K/128, M]) and fp32 per-128x128 weight scales ([N/128, K/128]).
+* ``fp8mx_gemm(A, a_scale_packed, B_prep, b_scale_packed, C)`` -- 1x32 ue8m0 scales, packed
+  once by ``fp8mx_pack_a_scale`` / ``fp8mx_prep_weights``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LIBRARY", "Fp8bsError", "lib", "fp8bs_version", "fp8bs_strerror",
+    "fp8bs_prep_weight_bytes", "fp8bs_prep_weights", "fp8bs_gemm",
+    "fp8mx_packed_scale_bytes", "fp8mx_pack_a_scale", "fp8mx_prep_weights", "fp8mx_gemm",
+    "prep_weights", "mx_prep_weights", "mx_pack_a_scale",
+]
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libfp8bs.so")
+
+# C ABI symbol table: name -> (restype, argtypes). Mirrors include/fp8bs.h.
+_vp, _int, _size = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "fp8bs_version": (_int, []),
+    "fp8bs_strerror": (ctypes.c_char_p, [_int]),
+    "fp8bs_prep_weight_bytes": (_size, [_int, _int]),
+    "fp8bs_prep_weights": (_int, [_vp, _vp, _int, _int, _vp]),
+    "fp8bs_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp]),
+    "fp8mx_packed_scale_bytes": (_size, [_int, _int]),
+    "fp8mx_pack_a_scale": (_int, [_vp, _vp, _int, _int, _vp]),
+    "fp8mx_prep_weights": (_int, [_vp, _vp, _vp, _vp, _int, _int, _vp]),
+    "fp8mx_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp]),
+}
+
+
+class Fp8bsError(RuntimeError):
+    """A libfp8bs call returned a non-zero status."""
+
+    def __init__(self, name: str, status: int):
+        self.status = status
+        super().__init__(f"{name} failed with status {status}: {fp8bs_strerror(status)}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIBRARY):
+        raise ImportError(
+            f"libfp8bs is not built ({LIBRARY} missing); build it with "
+            "`python -c 'import __graft_entry__ as g; g.build()'` from the repository root")
+    handle = ctypes.CDLL(LIBRARY)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(handle, name)
+        fn.restype = res
+        fn.argtypes = args
+    return handle
+
+
+lib = _load()
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libfp8bs takes device tensors only")
+    if not t.is_contiguous():
+        raise ValueError("libfp8bs takes contiguous tensors only")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(name: str, status: int) -> None:
+    if status != 0:
+        raise Fp8bsError(name, status)
+
+
+# ---- raw ABI, same names as include/fp8bs.h --------------------------------------------------
+
+def fp8bs_version() -> int:
+    return lib.fp8bs_version()
+
+
+def fp8bs_strerror(status: int) -> str:
+    return lib.fp8bs_strerror(status).decode()
+
+
+def fp8bs_prep_weight_bytes(N: int, K: int) -> int:
+    return lib.fp8bs_prep_weight_bytes(N, K)
+
+
+def fp8mx_packed_scale_bytes(rows: int, K: int) -> int:
+    return lib.fp8mx_packed_scale_bytes(rows, K)
+
+
+def fp8bs_prep_weights(B: torch.Tensor, B_prep: torch.Tensor, stream=None) -> None:
+    N, K = B.shape
+    _check("fp8bs_prep_weights", lib.fp8bs_prep_weights(_ptr(B), _ptr(B_prep), N, K, _stream(stream)))
+
+
+def fp8bs_gemm(A: torch.Tensor, a_scale: torch.Tensor, B_prep: torch.Tensor, b_scale: torch.Tensor,
+               C: torch.Tensor, stream=None) -> torch.Tensor:
+    """C[M,N] (bf16) from A [M,K] (uint8 e4m3 codes), a_scale [K/128, M] fp32, B_prep from
+    fp8bs_prep_weights of B [N,K], b_scale [N/128, K/128] fp32."""
+    M, K = A.shape
+    N = C.shape[1]
+    _check("fp8bs_gemm", lib.fp8bs_gemm(_ptr(A), _ptr(a_scale), _ptr(B_prep), _ptr(b_scale), _ptr(C),
+                                        M, N, K, _stream(stream)))
+    return C
+
+
+def fp8mx_pack_a_scale(a_e8m0: torch.Tensor, a_scale_packed: torch.Tensor, stream=None) -> None:
+    M, G = a_e8m0.shape
+    _check("fp8mx_pack_a_scale", lib.fp8mx_pack_a_scale(_ptr(a_e8m0), _ptr(a_scale_packed), M, G * 32,
+                                                        _stream(stream)))
+
+
+def fp8mx_prep_weights(B: torch.Tensor, b_e8m0: torch.Tensor, B_prep: torch.Tensor,
+                       b_scale_packed: torch.Tensor, stream=None) -> None:
+    N, K = B.shape
+    _check("fp8mx_prep_weights", lib.fp8mx_prep_weights(_ptr(B), _ptr(b_e8m0), _ptr(B_prep),
+                                                        _ptr(b_scale_packed), N, K, _stream(stream)))
+
+
+def fp8mx_gemm(A: torch.Tensor, a_scale_packed: torch.Tensor, B_prep: torch.Tensor,
+               b_scale_packed: torch.Tensor, C: torch.Tensor, stream=None) -> torch.Tensor:
+    M, K = A.shape
+    N = C.shape[1]
+    _check("fp8mx_gemm", lib.fp8mx_gemm(_ptr(A), _ptr(a_scale_packed), _ptr(B_prep), _ptr(b_scale_packed),
+                                        _ptr(C), M, N, K, _stream(stream)))
+    return C
+
+
+# ---- allocation helpers (torch owns the memory; the library never allocates) ----------------
+
+def prep_weights(B: torch.Tensor, stream=None) -> torch.Tensor:
+    """Prepared weight buffer for B [N,K] uint8 e4m3 codes (route BS)."""
+    N, K = B.shape
+    out = torch.empty(fp8bs_prep_weight_bytes(N, K), dtype=torch.uint8, device=B.device)
+    fp8bs_prep_weights(B, out, stream)
+    return out
+
+
+def mx_prep_weights(B: torch.Tensor, b_e8m0: torch.Tensor, stream=None):
+    """(prepared weights, packed weight scales) for route MX."""
+    N, K = B.shape
+    B_prep = torch.empty(fp8bs_prep_weight_bytes(N, K), dtype=torch.uint8, device=B.device)
+    packed = torch.empty(fp8mx_packed_scale_bytes(N, K), dtype=torch.uint8, device=B.device)
+    fp8mx_prep_weights(B, b_e8m0, B_prep, packed, stream)
+    return B_prep, packed
+
+
+def mx_pack_a_scale(a_e8m0: torch.Tensor, stream=None) -> torch.Tensor:
+    M, G = a_e8m0.shape
+    packed = torch.empty(fp8mx_packed_scale_bytes(M, G * 32), dtype=torch.uint8, device=a_e8m0.device)
+    fp8mx_pack_a_scale(a_e8m0, packed, stream)
+    return packed

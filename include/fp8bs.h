@@ -1,0 +1,120 @@
+/*
+ * fp8bs.h -- C ABI of the MI355X (gfx950) fp8 block-scaled GEMM library (libfp8bs.so).
+ *
+ * Two routes compute C[M,N] (bf16, row-major) from fp8 OCP e4m3 operands A[M,K] (activations)
+ * and B[N,K] (weights), both row-major with K contiguous:
+ *
+ *   route BS  fp8bs_gemm: fp32 block scales, one per 1x128 group of A (a_s[m,kb]) and one
+ *             per 128x128 block of B (b_s[nb,kb]):
+ *               C[m,n] = bf16( sum_kb a_s[m,kb] * b_s[n/128,kb] * sum_{k in kb} A[m,k]*B[n,k] )
+ *             The fp8 products run unscaled on the matrix cores and the fp32 scales are applied
+ *             in software to each 128-wide K block's partial sum, never folded into the
+ *             hardware's power-of-two scale operands (page "Flydsl Fp8 Blockscale Gemm",
+ *             Mechanism A; Procedure step 3).
+ *
+ *   route MX  fp8mx_gemm: ue8m0 (power-of-two) scales, one per 1x32 group along K for each
+ *             row of A and of B, applied by the scaled matrix-core instruction:
+ *               C[m,n] = bf16( sum_g 2^(ea[m,g]-127) * 2^(eb[n,g]-127) * sum_{k in g} A[m,k]*B[n,k] )
+ *             (page "aiter PR #6370", "Why it is faster").
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are device pointers unless stated otherwise; the caller owns every buffer.
+ *     The library never allocates, frees or keeps per-call state.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream). No call synchronises
+ *     the host, so calls may be captured into a HIP graph.
+ *   - Every call returns an fp8bs_status. Pointer, shape and alignment checks run on the host
+ *     before anything is launched; on failure nothing is enqueued and outputs are untouched.
+ *     Launch failures are reported as FP8BS_E_HIP. No call aborts or throws.
+ *   - Shapes that break a constraint are rejected, never padded (page "aiter PR #6370",
+ *     Constraints).
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP8BS_OK = 0,
+    FP8BS_E_NULL = 1,    /* a required pointer is NULL                                  */
+    FP8BS_E_SHAPE = 2,   /* M, N or K violates the route's constraints                   */
+    FP8BS_E_ALIGN = 3,   /* a pointer is not 16-byte aligned                             */
+    FP8BS_E_CONFIG = 4,  /* an explicit kernel configuration is invalid for the shape    */
+    FP8BS_E_HIP = 5      /* the HIP runtime reported an error when enqueueing the work   */
+} fp8bs_status;
+
+/* Version of this ABI (major * 10000 + minor * 100 + patch). */
+int fp8bs_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *fp8bs_strerror(int status);
+
+/* ------------------------------------------------------------------------------------------
+ * Weight preparation (one-time, untimed; page "Flydsl Fp8 Blockscale Gemm", Procedure steps
+ * 2 and 6: weights are laid out once at set-up and the buffers reused every call).
+ * ------------------------------------------------------------------------------------------ */
+
+/* Bytes of the prepared weight buffer for an N x K e4m3 weight (same for both routes). */
+size_t fp8bs_prep_weight_bytes(int N, int K);
+
+/* Lay out B [N,K] (e4m3, row-major) into B_prep, the opaque layout that fp8bs_gemm and
+ * fp8mx_gemm consume. B_prep must hold fp8bs_prep_weight_bytes(N, K) bytes and must not
+ * overlap B. Constraints: N % 64 == 0, K % 128 == 0, K >= 128; B and B_prep 16-byte aligned. */
+int fp8bs_prep_weights(const void *B, void *B_prep, int N, int K, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Route BS.
+ * ------------------------------------------------------------------------------------------ */
+
+/* C[M,N] = blockscaled(A, B).
+ *   A        [M, K] e4m3, row-major (lda = K).
+ *   a_scale  [K/128, M] fp32, K-block-major: a_scale[kb*M + m] scales A[m, 128kb : 128kb+128]
+ *            (page "Flydsl Fp8 Blockscale Gemm", Procedure step 6: the activation scale is fed
+ *            transposed, K block outermost).
+ *   B_prep   the output of fp8bs_prep_weights for B [N, K].
+ *   b_scale  [N/128, K/128] fp32, row-major: b_scale[nb*(K/128) + kb] scales B[128nb : 128nb+128,
+ *            128kb : 128kb+128].
+ *   C        [M, N] bf16, row-major (ldc = N); every element is written.
+ * Constraints: M >= 0 (M == 0 is a no-op), N % 128 == 0, K % 128 == 0, K >= 128, N >= 128;
+ * A, B_prep and C 16-byte aligned; a_scale and b_scale 4-byte aligned. Any M is accepted: the
+ * last row tile masks its stores. Results are bitwise deterministic run to run. */
+int fp8bs_gemm(const void *A, const float *a_scale, const void *B_prep, const float *b_scale,
+               void *C, int M, int N, int K, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Route MX.
+ * ------------------------------------------------------------------------------------------ */
+
+/* Bytes of a packed ue8m0 scale buffer for `rows` rows and K columns (K/32 scales per row). */
+size_t fp8mx_packed_scale_bytes(int rows, int K);
+
+/* Pack B's ue8m0 scales b_e8m0 [N, K/32] (uint8, biased by 127, row-major) into the
+ * K-block-major, four-to-a-dword layout the scaled instruction consumes (page "aiter PR
+ * #6370", "Why it is faster", second bullet), and lay out B as fp8bs_prep_weights does.
+ * Constraints: N % 64 == 0, K % 128 == 0, K >= 256. */
+int fp8mx_prep_weights(const void *B, const void *b_e8m0, void *B_prep, void *b_scale_packed,
+                       int N, int K, hipStream_t stream);
+
+/* Pack A's ue8m0 scales a_e8m0 [M, K/32] into a_scale_packed (fp8mx_packed_scale_bytes(M, K)
+ * bytes). Constraints: M % 64 == 0 (the packed group is 64 rows), K % 128 == 0, K >= 256. */
+int fp8mx_pack_a_scale(const void *a_e8m0, void *a_scale_packed, int M, int K, hipStream_t stream);
+
+/* C[M,N] = mx(A, B). A [M, K] e4m3 row-major; a_scale_packed from fp8mx_pack_a_scale;
+ * B_prep and b_scale_packed from fp8mx_prep_weights; C [M, N] bf16 row-major.
+ * Constraints: M % 64 == 0, N % 64 == 0, K % 128 == 0, K >= 256; A, B_prep, C and the packed
+ * scales 16-byte aligned. Crossing the two packed scale buffers is not detectable (they have
+ * the same size and type) and computes a wrong result rather than failing. */
+int fp8mx_gemm(const void *A, const void *a_scale_packed, const void *B_prep,
+               const void *b_scale_packed, void *C, int M, int N, int K, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */

@@ -1,0 +1,81 @@
+"""The C-ABI library loads and exports every function include/fp8bs.h declares, and the
+host-side validation (which runs before any HIP call) returns the documented codes. CPU only:
+no call here launches work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bs.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(fp8(?:bs|mx)_[a-z0-9_]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def fb():
+    import fp8_block_scaled_e4m3_amd as fb
+    return fb
+
+
+def test_header_declares_the_routes():
+    names = _declared()
+    for n in ("fp8bs_gemm", "fp8mx_gemm", "fp8bs_prep_weights", "fp8mx_prep_weights", "fp8mx_pack_a_scale"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(fb):
+    handle = ctypes.CDLL(fb.LIBRARY)
+    for name in _declared():
+        assert hasattr(handle, name), name
+        assert name in fb.SIGNATURES, f"binding lacks {name}"
+
+
+def test_version_and_strerror(fb):
+    assert fb.fp8bs_version() >= 10000
+    for code in range(6):
+        assert fb.fp8bs_strerror(code)
+    assert fb.fp8bs_strerror(99) == "unknown status"
+
+
+def test_sizes(fb):
+    assert fb.fp8bs_prep_weight_bytes(256, 512) == 256 * 512
+    assert fb.fp8mx_packed_scale_bytes(128, 512) == 128 * 16
+    assert fb.fp8bs_prep_weight_bytes(0, 512) == 0
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 100, 128), (16, 128, 100), (16, 128, 0), (-3, 128, 128), (16, 0, 128)])
+def test_bs_shape_rejected_before_any_launch(fb, M, N, K):
+    assert fb.lib.fp8bs_gemm(None, None, None, None, None, M, N, K, None) == 2
+
+
+def test_bs_null_rejected(fb):
+    assert fb.lib.fp8bs_gemm(None, None, None, None, None, 16, 128, 128, None) == 1
+
+
+def test_bs_misaligned_rejected(fb):
+    p = 0x1000
+    assert fb.lib.fp8bs_gemm(p + 4, p, p, p, p, 16, 128, 128, None) == 3
+    assert fb.lib.fp8bs_gemm(p, p + 2, p, p, p, 16, 128, 128, None) == 3
+
+
+@pytest.mark.parametrize("M,N,K", [(100, 128, 256), (128, 96, 256), (128, 128, 128), (128, 128, 200)])
+def test_mx_shape_rejected(fb, M, N, K):
+    assert fb.lib.fp8mx_gemm(None, None, None, None, None, M, N, K, None) == 2
+
+
+def test_mx_null_and_prep_validation(fb):
+    assert fb.lib.fp8mx_gemm(None, None, None, None, None, 64, 64, 256, None) == 1
+    assert fb.lib.fp8mx_pack_a_scale(None, None, 100, 256, None) == 2
+    assert fb.lib.fp8mx_prep_weights(None, None, None, None, 64, 128, None) == 2
+    assert fb.lib.fp8bs_prep_weights(None, None, 64, 128, None) == 1
+
+
+def test_zero_rows_is_accepted_without_pointers(fb):
+    assert fb.lib.fp8bs_gemm(None, None, None, None, None, 0, 128, 128, None) == 0

@@ -1,0 +1,69 @@
+"""Error paths of the C ABI on the GPU: rejected shapes and pointers return status codes,
+launch nothing and leave C untouched."""
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fb():
+    import fp8_block_scaled_e4m3_amd as fb
+    return fb
+
+
+def _bufs(M, N, K):
+    d = torch.device("cuda:0")
+    A = torch.zeros((M, K), dtype=torch.uint8, device=d)
+    sa = torch.ones((max(K // 128, 1), M), dtype=torch.float32, device=d)
+    B = torch.zeros((N, K), dtype=torch.uint8, device=d)
+    sb = torch.ones((max(N // 128, 1), max(K // 128, 1)), dtype=torch.float32, device=d)
+    C = torch.full((M, N), 7.0, dtype=torch.bfloat16, device=d)
+    return A, sa, B, sb, C
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 100, 128), (128, 128, 100), (128, 128, 0), (-1, 128, 128), (64, 64, 128)])
+def test_bs_rejects_bad_shapes(fb, M, N, K):
+    A, sa, B, sb, C = _bufs(max(M, 1), max(N, 1), max(K, 1))
+    st = fb.lib.fp8bs_gemm(A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(), C.data_ptr(),
+                           M, N, K, None)
+    torch.cuda.synchronize()
+    assert st == 2
+    assert torch.all(C == 7.0)
+
+
+def test_bs_rejects_null_and_misaligned(fb):
+    A, sa, B, sb, C = _bufs(128, 128, 256)
+    st = fb.lib.fp8bs_gemm(None, sa.data_ptr(), B.data_ptr(), sb.data_ptr(), C.data_ptr(), 128, 128, 256, None)
+    assert st == 1
+    st = fb.lib.fp8bs_gemm(A.data_ptr() + 8, sa.data_ptr(), B.data_ptr(), sb.data_ptr(), C.data_ptr(),
+                           120, 128, 256, None)
+    assert st == 3
+    torch.cuda.synchronize()
+    assert torch.all(C == 7.0)
+
+
+@pytest.mark.parametrize("M,N,K", [(100, 128, 256), (128, 96, 256), (128, 128, 128), (128, 128, 200)])
+def test_mx_rejects_bad_shapes(fb, M, N, K):
+    A, _, B, _, C = _bufs(M, N, K)
+    pa = torch.zeros(4096, dtype=torch.uint8, device=A.device)
+    st = fb.lib.fp8mx_gemm(A.data_ptr(), pa.data_ptr(), B.data_ptr(), pa.data_ptr(), C.data_ptr(),
+                           M, N, K, None)
+    torch.cuda.synchronize()
+    assert st == 2
+    assert torch.all(C == 7.0)
+
+
+def test_zero_rows_is_noop(fb):
+    A, sa, B, sb, C = _bufs(1, 128, 128)
+    assert fb.lib.fp8bs_gemm(A.data_ptr(), sa.data_ptr(), B.data_ptr(), sb.data_ptr(), C.data_ptr(),
+                             0, 128, 128, None) == 0
+    torch.cuda.synchronize()
+    assert torch.all(C == 7.0)
+
+
+def test_python_wrapper_raises(fb):
+    A, sa, B, sb, C = _bufs(128, 128, 256)
+    with pytest.raises(fb.Fp8bsError):
+        fb.fp8bs_gemm(A, sa, B, sb, torch.empty((128, 100), dtype=torch.bfloat16, device=A.device))

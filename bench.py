@@ -31,7 +31,7 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix-core peak (published), TFL
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published), GB/s
 METRIC = "fp8 blockscale GEMM TFLOP/s and % of MI355X dense fp8 MFMA peak, per shape"
 MAIN = "narrow_n"
-KERNEL_SOURCES = ["bs_gemm.hip", "mx_gemm.hip", "device.hpp"]
+KERNEL_SOURCES = ["gemm.hip", "device.hpp"]
 
 
 def log(*a):
@@ -256,7 +256,7 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                      "traffic": committed_traffic(MAIN),
-                     "kernel": "bs_gemm_kernel", "avg_launch_us": round(main_row["ev"] * 1e6, 2),
+                     "kernel": "gemm_kernel (route BS)", "avg_launch_us": round(main_row["ev"] * 1e6, 2),
                      "flop_per_launch": case.flops},
         "cpu_baseline": main_row["baseline"],
         "per_shape": per_shape,

@@ -24,6 +24,7 @@ __all__ = [
     "fp8bs_prep_weight_bytes", "fp8bs_prep_weights", "fp8bs_gemm",
     "fp8mx_packed_scale_bytes", "fp8mx_pack_a_scale", "fp8mx_prep_weights", "fp8mx_gemm",
     "prep_weights", "mx_prep_weights", "mx_pack_a_scale",
+    "Config", "ROUTE_BS", "ROUTE_MX", "fp8bs_select_config", "fp8bs_gemm_with_config", "fp8mx_gemm_with_config",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -41,7 +42,24 @@ SIGNATURES = {
     "fp8mx_pack_a_scale": (_int, [_vp, _vp, _int, _int, _vp]),
     "fp8mx_prep_weights": (_int, [_vp, _vp, _vp, _vp, _int, _int, _vp]),
     "fp8mx_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp]),
+    "fp8bs_select_config": (_int, [_int, _int, _int, _int, _vp]),
+    "fp8bs_gemm_with_config": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp, _vp]),
+    "fp8mx_gemm_with_config": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp, _vp]),
 }
+
+ROUTE_BS, ROUTE_MX = 0, 1
+
+
+class Config(ctypes.Structure):
+    """fp8bs_config of include/fp8bs.h."""
+    _fields_ = [(n, ctypes.c_int) for n in
+                ("block_m", "block_n", "waves_m", "waves_n", "stages", "group_m", "xcd_remap", "persistent")]
+
+    def as_dict(self) -> dict:
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+    def __repr__(self) -> str:
+        return f"Config({self.as_dict()})"
 
 
 class Fp8bsError(RuntimeError):
@@ -142,6 +160,30 @@ def fp8mx_gemm(A: torch.Tensor, a_scale_packed: torch.Tensor, B_prep: torch.Tens
     N = C.shape[1]
     _check("fp8mx_gemm", lib.fp8mx_gemm(_ptr(A), _ptr(a_scale_packed), _ptr(B_prep), _ptr(b_scale_packed),
                                         _ptr(C), M, N, K, _stream(stream)))
+    return C
+
+
+def fp8bs_select_config(route: int, M: int, N: int, K: int) -> Config:
+    cfg = Config()
+    _check("fp8bs_select_config", lib.fp8bs_select_config(route, M, N, K, ctypes.byref(cfg)))
+    return cfg
+
+
+def fp8bs_gemm_with_config(A, a_scale, B_prep, b_scale, C, config: Config, stream=None):
+    M, K = A.shape
+    N = C.shape[1]
+    _check("fp8bs_gemm_with_config",
+           lib.fp8bs_gemm_with_config(_ptr(A), _ptr(a_scale), _ptr(B_prep), _ptr(b_scale), _ptr(C), M, N, K,
+                                      ctypes.byref(config), _stream(stream)))
+    return C
+
+
+def fp8mx_gemm_with_config(A, a_scale_packed, B_prep, b_scale_packed, C, config: Config, stream=None):
+    M, K = A.shape
+    N = C.shape[1]
+    _check("fp8mx_gemm_with_config",
+           lib.fp8mx_gemm_with_config(_ptr(A), _ptr(a_scale_packed), _ptr(B_prep), _ptr(b_scale_packed), _ptr(C),
+                                      M, N, K, ctypes.byref(config), _stream(stream)))
     return C
 
 

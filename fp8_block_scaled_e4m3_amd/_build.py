@@ -18,13 +18,15 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(HERE, "libfp8bs.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "bs_gemm.hip", "mx_gemm.hip", "prep.hip"]
+SOURCES = ["api.hip", "gemm.hip", "prep.hip"]
 
 # Packed fp32 VALU instructions are disabled on purpose: ordinary float code only.
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-command-line-argument",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-command-line-argument",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
+    # keep matrix-core results in ordinary VGPRs: the software promote reads them with the VALU
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -8,16 +8,22 @@
 
 namespace {
 
-constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kVersion = 10100;  // 1.1.0
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? FP8BS_OK : FP8BS_E_HIP; }
 
+// The kernels address operands with 32-bit byte offsets.
+bool fits_offsets(int M, int N, int K)
+{
+    return (int64_t)M * K < (int64_t)1 << 31 && (int64_t)N * K < (int64_t)1 << 31;
+}
+
 // Shape rules of route BS: K in whole 128-wide blocks, N in whole 128-row weight blocks.
 int check_bs_shape(int M, int N, int K)
 {
-    if (M < 0 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0)
+    if (M < 0 || N < 128 || K < 128 || N % 128 != 0 || K % 128 != 0 || !fits_offsets(M, N, K))
         return FP8BS_E_SHAPE;
     return FP8BS_OK;
 }
@@ -26,8 +32,113 @@ int check_bs_shape(int M, int N, int K)
 // scale groups, K in whole 128-wide steps and at least two of them.
 int check_mx_shape(int M, int N, int K)
 {
-    if (M < 0 || M % 64 != 0 || N < 64 || N % 64 != 0 || K < 256 || K % 128 != 0)
+    if (M < 0 || M % 64 != 0 || N < 64 || N % 64 != 0 || K < 256 || K % 128 != 0 || !fits_offsets(M, N, K))
         return FP8BS_E_SHAPE;
+    return FP8BS_OK;
+}
+
+int find_variant(const fp8bs_config& c)
+{
+    for (int v = 0;; ++v) {
+        const fp8bs::VariantInfo* vi = fp8bs::variant_info(v);
+        if (!vi)
+            return -1;
+        if (vi->block_m == c.block_m && vi->block_n == c.block_n && vi->waves_m == c.waves_m &&
+            vi->waves_n == c.waves_n && vi->stages == c.stages)
+            return v;
+    }
+}
+
+fp8bs_config make_config(int variant, int group_m, int xcd_remap, int persistent)
+{
+    const fp8bs::VariantInfo* vi = fp8bs::variant_info(variant);
+    fp8bs_config c;
+    c.block_m = vi->block_m;
+    c.block_n = vi->block_n;
+    c.waves_m = vi->waves_m;
+    c.waves_n = vi->waves_n;
+    c.stages = vi->stages;
+    c.group_m = group_m;
+    c.xcd_remap = xcd_remap;
+    c.persistent = persistent;
+    return c;
+}
+
+// Shape-driven choice of the workgroup tile (page "Flydsl Fp8 Blockscale Gemm", Per-shape
+// recipes: selection by (M, N, K) alone, never by layer). Prefer the 256x256 tile when it
+// still gives at least two workgroups per CU, else the 128x256 / 256x128 tiles when they fill
+// the 256 CUs, else 128x128 (or 128x64 for MX with N not a multiple of 128).
+fp8bs_config select(int route, int M, int N, int K)
+{
+    (void)K;
+    const int kCUs = 256;
+    auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * (N / bn); };
+    if (route == fp8bs::kRouteMX && N % 128 != 0)
+        return make_config(7, 4, 1, 1);
+    if (N % 256 == 0 && tiles(256, 256) >= 2 * kCUs)
+        return make_config(2, 4, 1, 1);
+    if (tiles(256, 128) >= kCUs)
+        return make_config(6, 4, 1, 1);
+    if (N % 256 == 0 && tiles(128, 256) >= kCUs)
+        return make_config(5, 4, 1, 1);
+    return make_config(0, 4, 1, 1);
+}
+
+int check_config(int route, const fp8bs_config* c, int N, fp8bs::GemmConfig* out)
+{
+    if (!c)
+        return FP8BS_E_NULL;
+    const int v = find_variant(*c);
+    if (v < 0 || !fp8bs::variant_supports(route, v) || c->group_m < 1 || N % c->block_n != 0 ||
+        (c->xcd_remap != 0 && c->xcd_remap != 1) || (c->persistent != 0 && c->persistent != 1))
+        return FP8BS_E_CONFIG;
+    out->variant = v;
+    out->group_m = c->group_m;
+    out->xcd_remap = c->xcd_remap;
+    out->persistent = c->persistent;
+    return FP8BS_OK;
+}
+
+int run(int route, const void* A, const void* a_scale, const void* B_prep, const void* b_scale, void* C,
+        int M, int N, int K, const fp8bs_config* cfg, hipStream_t stream)
+{
+    fp8bs::GemmConfig gc;
+    int st = check_config(route, cfg, N, &gc);
+    if (st != FP8BS_OK)
+        return st;
+    fp8bs::GemmArgs args{A, a_scale, B_prep, b_scale, C, M, N, K, stream};
+    return hip_status(fp8bs::launch_gemm(route, args, gc));
+}
+
+int check_bs_args(const void* A, const float* a_scale, const void* B_prep, const float* b_scale, void* C,
+                  int M, int N, int K)
+{
+    int st = check_bs_shape(M, N, K);
+    if (st != FP8BS_OK)
+        return st;
+    if (M == 0)
+        return -1;  // nothing to do
+    if (!A || !a_scale || !B_prep || !b_scale || !C)
+        return FP8BS_E_NULL;
+    if (!aligned(A, 16) || !aligned(B_prep, 16) || !aligned(C, 16) || !aligned(a_scale, 4) ||
+        !aligned(b_scale, 4))
+        return FP8BS_E_ALIGN;
+    return FP8BS_OK;
+}
+
+int check_mx_args(const void* A, const void* a_scale_packed, const void* B_prep, const void* b_scale_packed,
+                  void* C, int M, int N, int K)
+{
+    int st = check_mx_shape(M, N, K);
+    if (st != FP8BS_OK)
+        return st;
+    if (M == 0)
+        return -1;
+    if (!A || !a_scale_packed || !B_prep || !b_scale_packed || !C)
+        return FP8BS_E_NULL;
+    if (!aligned(A, 16) || !aligned(B_prep, 16) || !aligned(C, 16) || !aligned(a_scale_packed, 16) ||
+        !aligned(b_scale_packed, 16))
+        return FP8BS_E_ALIGN;
     return FP8BS_OK;
 }
 
@@ -44,7 +155,7 @@ const char* fp8bs_strerror(int status)
     case FP8BS_E_NULL: return "a required pointer is NULL";
     case FP8BS_E_SHAPE: return "M, N or K violates the route's shape constraints";
     case FP8BS_E_ALIGN: return "a pointer is not suitably aligned (16 bytes for tensors, 4 for fp32 scales)";
-    case FP8BS_E_CONFIG: return "invalid kernel configuration for this shape";
+    case FP8BS_E_CONFIG: return "invalid kernel configuration for this shape or route";
     case FP8BS_E_HIP: return "the HIP runtime reported an error while enqueueing work";
     default: return "unknown status";
     }
@@ -59,30 +170,45 @@ size_t fp8bs_prep_weight_bytes(int N, int K)
 
 int fp8bs_prep_weights(const void* B, void* B_prep, int N, int K, hipStream_t stream)
 {
-    if (!B || !B_prep)
-        return FP8BS_E_NULL;
     if (N < 64 || N % 64 != 0 || K < 128 || K % 128 != 0)
         return FP8BS_E_SHAPE;
+    if (!B || !B_prep)
+        return FP8BS_E_NULL;
     if (!aligned(B, 16) || !aligned(B_prep, 16))
         return FP8BS_E_ALIGN;
     return hip_status(fp8bs::launch_prep_weights(B, B_prep, N, K, stream));
 }
 
-int fp8bs_gemm(const void* A, const float* a_scale, const void* B_prep, const float* b_scale,
-               void* C, int M, int N, int K, hipStream_t stream)
+int fp8bs_select_config(int route, int M, int N, int K, fp8bs_config* out)
 {
-    int st = check_bs_shape(M, N, K);
+    if (!out)
+        return FP8BS_E_NULL;
+    if (route != FP8BS_ROUTE_BS && route != FP8BS_ROUTE_MX)
+        return FP8BS_E_CONFIG;
+    int st = route == FP8BS_ROUTE_BS ? check_bs_shape(M, N, K) : check_mx_shape(M, N, K);
     if (st != FP8BS_OK)
         return st;
-    if (M == 0)
-        return FP8BS_OK;
-    if (!A || !a_scale || !B_prep || !b_scale || !C)
-        return FP8BS_E_NULL;
-    if (!aligned(A, 16) || !aligned(B_prep, 16) || !aligned(C, 16) || !aligned(a_scale, 4) ||
-        !aligned(b_scale, 4))
-        return FP8BS_E_ALIGN;
-    fp8bs::BsArgs args{A, a_scale, B_prep, b_scale, C, M, N, K, stream};
-    return hip_status(fp8bs::launch_bs(args));
+    *out = select(route, M, N, K);
+    return FP8BS_OK;
+}
+
+int fp8bs_gemm(const void* A, const float* a_scale, const void* B_prep, const float* b_scale, void* C,
+               int M, int N, int K, hipStream_t stream)
+{
+    int st = check_bs_args(A, a_scale, B_prep, b_scale, C, M, N, K);
+    if (st != FP8BS_OK)
+        return st < 0 ? FP8BS_OK : st;
+    const fp8bs_config cfg = select(fp8bs::kRouteBS, M, N, K);
+    return run(fp8bs::kRouteBS, A, a_scale, B_prep, b_scale, C, M, N, K, &cfg, stream);
+}
+
+int fp8bs_gemm_with_config(const void* A, const float* a_scale, const void* B_prep, const float* b_scale,
+                           void* C, int M, int N, int K, const fp8bs_config* config, hipStream_t stream)
+{
+    int st = check_bs_args(A, a_scale, B_prep, b_scale, C, M, N, K);
+    if (st != FP8BS_OK)
+        return st < 0 ? FP8BS_OK : st;
+    return run(fp8bs::kRouteBS, A, a_scale, B_prep, b_scale, C, M, N, K, config, stream);
 }
 
 size_t fp8mx_packed_scale_bytes(int rows, int K)
@@ -102,11 +228,11 @@ int fp8mx_pack_a_scale(const void* a_e8m0, void* a_scale_packed, int M, int K, h
         return FP8BS_E_NULL;
     if (!aligned(a_scale_packed, 16))
         return FP8BS_E_ALIGN;
-    return hip_status(fp8bs::launch_pack_scales(a_e8m0, a_scale_packed, M, K, stream));
+    return hip_status(fp8bs::launch_pack_scales(a_e8m0, a_scale_packed, M, K, 0, stream));
 }
 
-int fp8mx_prep_weights(const void* B, const void* b_e8m0, void* B_prep, void* b_scale_packed,
-                       int N, int K, hipStream_t stream)
+int fp8mx_prep_weights(const void* B, const void* b_e8m0, void* B_prep, void* b_scale_packed, int N, int K,
+                       hipStream_t stream)
 {
     if (N < 64 || N % 64 != 0 || K < 256 || K % 128 != 0)
         return FP8BS_E_SHAPE;
@@ -117,24 +243,27 @@ int fp8mx_prep_weights(const void* B, const void* b_e8m0, void* B_prep, void* b_
     hipError_t e = fp8bs::launch_prep_weights(B, B_prep, N, K, stream);
     if (e != hipSuccess)
         return FP8BS_E_HIP;
-    return hip_status(fp8bs::launch_pack_scales(b_e8m0, b_scale_packed, N, K, stream));
+    return hip_status(fp8bs::launch_pack_scales(b_e8m0, b_scale_packed, N, K, 1, stream));
 }
 
-int fp8mx_gemm(const void* A, const void* a_scale_packed, const void* B_prep,
-               const void* b_scale_packed, void* C, int M, int N, int K, hipStream_t stream)
+int fp8mx_gemm(const void* A, const void* a_scale_packed, const void* B_prep, const void* b_scale_packed,
+               void* C, int M, int N, int K, hipStream_t stream)
 {
-    int st = check_mx_shape(M, N, K);
+    int st = check_mx_args(A, a_scale_packed, B_prep, b_scale_packed, C, M, N, K);
     if (st != FP8BS_OK)
-        return st;
-    if (M == 0)
-        return FP8BS_OK;
-    if (!A || !a_scale_packed || !B_prep || !b_scale_packed || !C)
-        return FP8BS_E_NULL;
-    if (!aligned(A, 16) || !aligned(B_prep, 16) || !aligned(C, 16) ||
-        !aligned(a_scale_packed, 16) || !aligned(b_scale_packed, 16))
-        return FP8BS_E_ALIGN;
-    fp8bs::MxArgs args{A, a_scale_packed, B_prep, b_scale_packed, C, M, N, K, stream};
-    return hip_status(fp8bs::launch_mx(args));
+        return st < 0 ? FP8BS_OK : st;
+    const fp8bs_config cfg = select(fp8bs::kRouteMX, M, N, K);
+    return run(fp8bs::kRouteMX, A, a_scale_packed, B_prep, b_scale_packed, C, M, N, K, &cfg, stream);
+}
+
+int fp8mx_gemm_with_config(const void* A, const void* a_scale_packed, const void* B_prep,
+                           const void* b_scale_packed, void* C, int M, int N, int K, const fp8bs_config* config,
+                           hipStream_t stream)
+{
+    int st = check_mx_args(A, a_scale_packed, B_prep, b_scale_packed, C, M, N, K);
+    if (st != FP8BS_OK)
+        return st < 0 ? FP8BS_OK : st;
+    return run(fp8bs::kRouteMX, A, a_scale_packed, B_prep, b_scale_packed, C, M, N, K, config, stream);
 }
 
 }  // extern "C"

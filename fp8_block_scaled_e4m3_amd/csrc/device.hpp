@@ -51,4 +51,14 @@ __device__ __forceinline__ uint32_t lds_tile_offset(uint32_t row, uint32_t chunk
     return row * 128u + ((chunk ^ (row & 7u)) << 4);
 }
 
+// Row order of the prepared weight buffer inside each 64-row window: prepared row
+// rho = 16j + 4a + r (sub-tile j, output lane group a, register r of the swap-AB result) holds
+// weight row 32*(j/2) + 8a + 4*(j%2) + r. With this order the result registers of sub-tiles
+// j and j+1 (j even) in lane group a are output columns 32*(j/2) + 8a .. +7 of the window.
+__host__ __device__ __forceinline__ int weight_row_perm(int rho)
+{
+    const int j = rho >> 4, a = (rho >> 2) & 3, r = rho & 3;
+    return 32 * (j >> 1) + 8 * a + 4 * (j & 1) + r;
+}
+
 }  // namespace fp8bs

@@ -1,0 +1,494 @@
+// gemm.hip -- the two GEMM routes of libfp8bs on one gfx950 mainloop.
+//
+// Route BS (page "Flydsl Fp8 Blockscale Gemm", Mechanism A): fp32 block scales cannot be
+// expressed by the matrix core's power-of-two scale operands, so each 128-wide K block of a
+// 16x16 output tile is one UNSCALED v_mfma_f32_16x16x128_f8f6f4 into a fresh fp32 partial
+// (four VGPRs), immediately "promoted": acc += partial * (a_s[m,kb] * b_s[n/128,kb]). The
+// promote is 4 fp32 FMAs per instruction, interleaved by the compiler with the following
+// matrix instructions so the vector ALU works while the matrix core runs.
+//
+// Route MX (page "aiter PR #6370", "Why it is faster"): the 1x32 ue8m0 scales ride in the
+// scale operands of v_mfma_scale_f32_16x16x128_f8f6f4, accumulating straight into acc.
+//
+// Work decomposition (shared by both routes):
+//  * Persistent workgroups: one per CU slot, each walking a list of BM x BN output tiles. The
+//    (tile, 128-wide K block) pairs of a workgroup form one stream of steps; the operands of
+//    step s + STAGES - 1 are requested while step s computes, across tile boundaries, so a new
+//    tile starts on data that is already in LDS and a finished tile's C stores drain while
+//    the next tile computes.
+//  * Operands move global -> LDS with buffer_load_dwordx4 ... lds (no staging registers; the
+//    K advance is a scalar offset) into a ring of STAGES LDS buffers, one barrier per step.
+//    The block scales of the step travel in the same buffer (buffer_load_dword ... lds), so
+//    every wave issues the same number of loads per step and a single vmcnt wait covers them.
+//  * Each wave computes a TM x TN sub-tile with the weights as the first matrix operand
+//    (swap-AB), so every lane owns four consecutive columns of one output row and stores
+//    8 contiguous bytes (page "aiter PR #6370", "Why it is faster", first bullet).
+//  * Tiles are handed out so that the workgroups running at the same time on one XCD (each
+//    XCD has its own L2) work on neighbouring tiles (page "Flydsl Fp8 Blockscale Gemm",
+//    Mechanism B: XCD-aware rasterisation).
+//
+// LDS layout of one stage: [A: BM rows x 128 B][B: BN rows x 128 B][A scales][B scales]. The
+// 16-byte chunks of a row r are XOR-swizzled with ((r >> 1) & 7): the sixteen lanes that read
+// the same chunk of sixteen consecutive rows fall on sixteen distinct 16-byte bank groups.
+#include "device.hpp"
+#include "launch.hpp"
+
+#include <type_traits>
+#include <utility>
+
+namespace fp8bs {
+
+__device__ __forceinline__ uint32_t swz(uint32_t row) { return (row >> 1) & 7u; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+constexpr int kLdsCapacity = 160 * 1024;
+
+template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES>
+struct Tile {
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kThreads = kWaves * 64;
+    static constexpr int TM = BM / WM;
+    static constexpr int TN = BN / WN;
+    static constexpr int SI = TM / 16;
+    static constexpr int SJ = TN / 16;
+    static constexpr int kABytes = BM * 128;
+    static constexpr int kBBytes = BN * 128;
+    static constexpr int kSABytes = BM * 4;                           // fp32 per row / packed dword per row
+    static constexpr int kSBBytes = ROUTE == kRouteBS ? 256 : BN * 4;  // BS: <= 64 weight-block scales
+    static constexpr int kStageBytes = kABytes + kBBytes + kSABytes + kSBBytes;
+    static constexpr int kLoadsA = BM / 8 / kWaves;  // 1 KB (8-row) loads per wave per step
+    static constexpr int kLoadsB = BN / 8 / kWaves;
+    static constexpr int kScaleLoadsA = BM / 64;     // 256-byte loads
+    static constexpr int kScaleLoadsB = ROUTE == kRouteBS ? 1 : BN / 64;
+    static constexpr int kScaleLoads = kScaleLoadsA + kScaleLoadsB;
+    static constexpr int kLoadsS = (kScaleLoads + kWaves - 1) / kWaves;
+    static constexpr int kLoadsPerStep = kLoadsA + kLoadsB + kLoadsS;
+    static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "whole 8-row groups per wave");
+    static_assert(BM % 64 == 0 && TM % 16 == 0 && TN % 64 == 0, "16x16 sub-tiles, 64-row scale loads, "
+                  "whole 64-column windows of the prepared weight order per wave");
+    static_assert(ROUTE == kRouteMX ? (TM % 64 == 0 && TN % 64 == 0) : (TN <= 128 && 128 % TN == 0),
+                  "MX: whole 64-row packed scale groups; BS: a wave's columns in one weight-scale block");
+    static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
+    static_assert(STAGES * kStageBytes <= kLdsCapacity, "LDS capacity");
+    static_assert(kLoadsPerStep * (STAGES - 1) <= 63, "vmcnt range");
+};
+
+// s_waitcnt with only a vmcnt limit (expcnt and lgkmcnt left unconstrained).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Tile u of the persistent order -> output tile (tm, tn). Workgroup ids are dispatched
+// round-robin over the 8 XCDs, so with a grid that is a multiple of 8, tile u runs on XCD u % 8.
+// With xcd_remap, XCD x owns the contiguous range [x*T/8, (x+1)*T/8) of the tile order, and the
+// workgroups of one XCD walk it together. The order visits group_m tile rows at a time, row
+// index fastest, so a window of concurrently running tiles is a compact block of the grid.
+__device__ __forceinline__ void tile_of(int u, int tiles_m, int tiles_n, int group_m, int xcd_remap,
+                                        int& tm, int& tn)
+{
+    const int T = tiles_m * tiles_n;
+    int t = u;
+    if (xcd_remap && (T & 7) == 0)
+        t = (u & 7) * (T >> 3) + (u >> 3);
+    const int per_group = group_m * tiles_n;
+    const int g = t / per_group;
+    const int first_m = g * group_m;
+    const int gm = min(tiles_m - first_m, group_m);
+    const int r = t - g * per_group;
+    tm = first_m + r % gm;
+    tn = r / gm;
+}
+
+// Route MX inner block: acc[I][J] += scaled(B_J, A_I) for all sub-tiles, with the op_sel
+// byte of each packed scale dword chosen at compile time (sub-tile index mod 4).
+template <int I, int J, int SI, int SJ, int GA, int GB>
+__device__ __forceinline__ void mx_rows(v4f (&acc)[SI][SJ], const v8i (&af)[SI], const v8i& bf,
+                                        const int (&sa)[GA], const int (&sb)[GB])
+{
+    if constexpr (I < SI) {
+        // weights first: the weight scale byte of sub-tile J, the activation byte of sub-tile I
+        acc[I][J] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[I], acc[I][J], kFmtE4M3, kFmtE4M3,
+                                                                     J & 3, sb[J / 4], I & 3, sa[I / 4]);
+        mx_rows<I + 1, J>(acc, af, bf, sa, sb);
+    }
+}
+
+template <int J, int SI, int SJ, int GA, int GB, typename Frag>
+__device__ __forceinline__ void mx_cols(v4f (&acc)[SI][SJ], const v8i (&af)[SI], const int (&sa)[GA],
+                                        const int (&sb)[GB], const uint8_t* sB, Frag& frag)
+{
+    if constexpr (J < SJ) {
+        const v8i bf = frag(sB + J * 16 * 128);
+        mx_rows<0, J>(acc, af, bf, sa, sb);
+        mx_cols<J + 1>(acc, af, sa, sb, sB, frag);
+    }
+}
+
+template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES>
+__global__ void __launch_bounds__(WM * WN * 64)
+gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
+            const uint8_t* __restrict__ B, const void* __restrict__ b_scale,
+            uint16_t* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
+            int group_m, int xcd_remap)
+{
+    using T = Tile<ROUTE, BM, BN, WM, WN, STAGES>;
+    // One LDS array per stage: the stage of every read is known at compile time, so the
+    // compiler can tell LDS-DMA writes to one stage from reads of another and adds no waits.
+    __shared__ __attribute__((aligned(1024))) uint8_t st0[T::kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st1[T::kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t st2[STAGES > 2 ? T::kStageBytes : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t st3[STAGES > 3 ? T::kStageBytes : 16];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave % WM;
+    const int wn = wave / WM;
+    const int KB = K >> 7;
+    const int T_total = tiles_m * tiles_n;
+    const int grid = gridDim.x;
+    // number of tiles this workgroup owns, and the length of its step stream
+    const int my_tiles = (int)blockIdx.x < T_total ? (T_total - 1 - (int)blockIdx.x) / grid + 1 : 0;
+    const int total = my_tiles * KB;
+
+    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0x7FFFFFFF, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, 0x7FFFFFFF, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsSA =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a_scale, (short)0, 0x7FFFFFFF, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rsSB =
+        __builtin_amdgcn_make_buffer_rsrc((void*)b_scale, (short)0, 0x7FFFFFFF, 0x00020000);
+
+    // ---- per-tile load descriptors (recomputed when the stream enters a new tile) ---------
+    // A wave's load g covers 8 rows (1 KB): lane l writes physical chunk l&7 of row l>>3, which
+    // holds logical K chunk (l&7) ^ swz(row); rows past M re-read row M-1 (never stored).
+    uint32_t voffA[T::kLoadsA];
+    uint32_t voffB[T::kLoadsB];
+    uint32_t voffS[T::kLoadsS];  // scale loads: byte offset without the K-block term
+    uint32_t kstrS[T::kLoadsS];  // bytes per K block of that scale array
+    int load_tile = -1;          // tile index (in this workgroup's list) the descriptors describe
+    auto setup_loads = [&](int i) {
+        int tm, tn;
+        tile_of((int)blockIdx.x + i * grid, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+#pragma unroll
+        for (int g = 0; g < T::kLoadsA; ++g) {
+            const int row = (wave * T::kLoadsA + g) * 8 + (lane >> 3);
+            const int m = min(m0 + row, M - 1);
+            voffA[g] = (uint32_t)m * (uint32_t)K + ((((uint32_t)lane & 7u) ^ swz(row)) << 4);
+        }
+#pragma unroll
+        for (int g = 0; g < T::kLoadsB; ++g) {
+            const int row = (wave * T::kLoadsB + g) * 8 + (lane >> 3);
+            voffB[g] = (uint32_t)(n0 + row) * (uint32_t)K + ((((uint32_t)lane & 7u) ^ swz(row)) << 4);
+        }
+#pragma unroll
+        for (int g = 0; g < T::kLoadsS; ++g) {
+            const int u = min(wave * T::kLoadsS + g, T::kScaleLoads - 1);
+            if (u < T::kScaleLoadsA) {
+                if constexpr (ROUTE == kRouteBS) {  // a_scale[kb*M + m], fp32
+                    voffS[g] = (uint32_t)min(m0 + 64 * u + lane, M - 1) * 4u;
+                } else {  // packed dword ((kb*M/64 + group)*64 + lane)
+                    voffS[g] = ((uint32_t)min((m0 >> 6) + u, (M >> 6) - 1) * 64u + (uint32_t)lane) * 4u;
+                }
+                kstrS[g] = (uint32_t)M * 4u;
+            } else {
+                if constexpr (ROUTE == kRouteBS) {  // b_scale[nb*KB + kb], fp32
+                    voffS[g] = (uint32_t)((n0 >> 7) + min(lane, (BN + 127) / 128 - 1)) * (uint32_t)KB * 4u;
+                    kstrS[g] = 4u;
+                } else {
+                    voffS[g] = ((uint32_t)((n0 >> 6) + (u - T::kScaleLoadsA)) * 64u + (uint32_t)lane) * 4u;
+                    kstrS[g] = (uint32_t)N * 4u;
+                }
+            }
+        }
+        load_tile = i;
+    };
+    auto issue_loads = [&](lds_u8* st, int step) {
+        const int i = step / KB;
+        const int kb = step - i * KB;
+        if (i != load_tile)
+            setup_loads(i);
+        const int koff = kb * 128;
+        lds_u8* sA = st;
+        lds_u8* sB = st + T::kABytes;
+        lds_u8* sS = st + T::kABytes + T::kBBytes;
+#pragma unroll
+        for (int g = 0; g < T::kLoadsA; ++g)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(sA + (wave * T::kLoadsA + g) * 1024), 16,
+                                                     (int)voffA[g], koff, 0, 0);
+#pragma unroll
+        for (int g = 0; g < T::kLoadsB; ++g)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void*)(sB + (wave * T::kLoadsB + g) * 1024), 16,
+                                                     (int)voffB[g], koff, 0, 0);
+#pragma unroll
+        for (int g = 0; g < T::kLoadsS; ++g) {
+            const int u = min(wave * T::kLoadsS + g, T::kScaleLoads - 1);  // uniform
+            const int soff = kb * (int)kstrS[g];
+            if (u < T::kScaleLoadsA)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsSA, (lds_void*)(sS + u * 256), 4, (int)voffS[g], soff, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsSB, (lds_void*)(sS + T::kSABytes + (u - T::kScaleLoadsA) * 256),
+                                                         4, (int)voffS[g], soff, 0, 0);
+        }
+    };
+
+    v4f acc[T::SI][T::SJ];
+#pragma unroll
+    for (int i = 0; i < T::SI; ++i)
+#pragma unroll
+        for (int j = 0; j < T::SJ; ++j)
+            acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int frow = lane & 15;
+    const uint32_t q = (uint32_t)lane >> 4;
+    // this lane's LDS byte offsets of chunk q and chunk q+4 for a row with (row & 15) == frow
+    const uint32_t c_lo = ((q ^ swz(frow)) << 4) + frow * 128u;
+    const uint32_t c_hi = (((q + 4u) ^ swz(frow)) << 4) + frow * 128u;
+    auto frag = [&](const uint8_t* base) -> v8i {
+        const v4i lo = *(const v4i*)(base + c_lo);
+        const v4i hi = *(const v4i*)(base + c_hi);
+        return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    };
+
+    // ---- epilogue: fp32 -> bf16 (nearest even) -------------------------------------------
+    // The prepared weight rows are ordered so that sub-tiles j and j+1 (j even) hand lane
+    // group q output columns 32*(j/2) + 8q .. +7 of the wave's 64-column window: one 16-byte
+    // store per lane and pair, sixteen rows x 64 contiguous bytes per store instruction.
+    auto store_tile = [&](int i) {
+        int tm, tn;
+        tile_of((int)blockIdx.x + i * grid, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
+        const int mbase = tm * BM + wm * T::TM + frow;
+        const int nbase = tn * BN + wn * T::TN + 8 * (int)q;
+#pragma unroll
+        for (int si = 0; si < T::SI; ++si) {
+            const int m = mbase + 16 * si;
+            if (m < M) {
+                uint16_t* crow = C + (size_t)m * N + nbase;
+#pragma unroll
+                for (int sj = 0; sj < T::SJ; sj += 2) {
+                    const v4f lo = acc[si][sj];
+                    const v4f hi = acc[si][sj + 1];
+                    v4i packed;
+                    packed.x = (int)pack_bf16x2(lo.x, lo.y);
+                    packed.y = (int)pack_bf16x2(lo.z, lo.w);
+                    packed.z = (int)pack_bf16x2(hi.x, hi.y);
+                    packed.w = (int)pack_bf16x2(hi.z, hi.w);
+                    *(v4i*)(crow + 32 * (sj >> 1)) = packed;
+                }
+            }
+#pragma unroll
+            for (int sj = 0; sj < T::SJ; ++sj)
+                acc[si][sj] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+
+    // ---- compute one step from a stage ----------------------------------------------------
+    auto compute = [&](const uint8_t* st) {
+        const uint8_t* sA = st + (wm * T::TM) * 128;
+        const uint8_t* sB = st + T::kABytes + (wn * T::TN) * 128;
+        const uint8_t* sS = st + T::kABytes + T::kBBytes;
+        v8i af[T::SI];
+#pragma unroll
+        for (int i = 0; i < T::SI; ++i)
+            af[i] = frag(sA + i * 16 * 128);
+        if constexpr (ROUTE == kRouteBS) {
+            const float* sa = (const float*)sS + wm * T::TM + frow;
+            const float sb = ((const float*)(sS + T::kSABytes))[(wn * T::TN) >> 7];
+            float s[T::SI];
+#pragma unroll
+            for (int i = 0; i < T::SI; ++i)
+                s[i] = sa[16 * i] * sb;
+#pragma unroll
+            for (int j = 0; j < T::SJ; ++j) {
+                const v8i bf = frag(sB + j * 16 * 128);
+#pragma unroll
+                for (int i = 0; i < T::SI; ++i) {
+                    const v4f p = mfma_f8(bf, af[i], v4f{0.f, 0.f, 0.f, 0.f});
+                    acc[i][j] += p * s[i];
+                }
+            }
+        } else {
+            constexpr int GA = (T::SI + 3) / 4;
+            constexpr int GB = (T::SJ + 3) / 4;
+            int sa[GA];
+            int sb[GB];
+#pragma unroll
+            for (int g = 0; g < GA; ++g)
+                sa[g] = ((const int*)sS)[(wm * T::TM / 64 + g) * 64 + lane];
+#pragma unroll
+            for (int g = 0; g < GB; ++g)
+                sb[g] = ((const int*)(sS + T::kSABytes))[(wn * T::TN / 64 + g) * 64 + lane];
+            // op_sel must be a constant: walk the sub-tiles with compile-time indices.
+            mx_cols<0>(acc, af, sa, sb, sB, frag);
+        }
+    };
+
+    // ---- the step stream ---------------------------------------------------------------------
+    // Before step s computes, its loads (issued STAGES-1 steps earlier) must have landed for
+    // every wave. Loads complete in order among themselves but not in order with the C stores
+    // of an epilogue, so right after an epilogue the wait is for everything.
+    int stores_pending = 0;
+    auto step = [&](auto S, int s) {
+        constexpr int kS = decltype(S)::value;
+        constexpr int kNext = (kS + STAGES - 1) % STAGES;
+        uint8_t* cur = kS == 0 ? st0 : kS == 1 ? st1 : kS == 2 ? st2 : st3;
+        uint8_t* nxt = kNext == 0 ? st0 : kNext == 1 ? st1 : kNext == 2 ? st2 : st3;
+        const int ahead = min(STAGES - 2, total - 1 - s);  // load groups issued after step s's
+        if (stores_pending || ahead <= 0) {
+            wait_vmcnt<0>();
+        } else if (ahead == 1) {
+            wait_vmcnt<T::kLoadsPerStep>();
+        } else {
+            wait_vmcnt<(STAGES > 3 ? 2 : 1) * T::kLoadsPerStep>();
+        }
+        stores_pending = 0;
+        __builtin_amdgcn_s_barrier();
+        if (s + STAGES - 1 < total)
+            issue_loads((lds_u8*)nxt, s + STAGES - 1);
+        compute(cur);
+        const int i = s / KB;
+        if (s - i * KB == KB - 1) {
+            store_tile(i);
+            stores_pending = 1;
+        }
+    };
+
+    if (0 < total)
+        issue_loads((lds_u8*)st0, 0);
+    if (STAGES > 2 && 1 < total)
+        issue_loads((lds_u8*)st1, 1);
+    if (STAGES > 3 && 2 < total)
+        issue_loads((lds_u8*)st2, 2);
+    for (int s = 0; s < total; s += STAGES) {
+        step(std::integral_constant<int, 0>{}, s);
+        if (s + 1 < total)
+            step(std::integral_constant<int, 1>{}, s + 1);
+        if constexpr (STAGES > 2) {
+            if (s + 2 < total)
+                step(std::integral_constant<int, 2>{}, s + 2);
+        }
+        if constexpr (STAGES > 3) {
+            if (s + 3 < total)
+                step(std::integral_constant<int, 3>{}, s + 3);
+        }
+    }
+}
+
+// ---- host side ---------------------------------------------------------------------------
+
+int device_cus()
+{
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES>
+static hipError_t launch_tile(const GemmArgs& a, const GemmConfig& c)
+{
+    using T = Tile<ROUTE, BM, BN, WM, WN, STAGES>;
+    // workgroups that fit on one CU at once (LDS and registers), once per instantiation
+    static const int per_cu = [] {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_kernel<ROUTE, BM, BN, WM, WN, STAGES>,
+                                                         T::kThreads, 0) != hipSuccess || n < 1)
+            n = 1;
+        return n;
+    }();
+    const int tiles_m = (a.M + BM - 1) / BM;
+    const int tiles_n = a.N / BN;
+    const int T_total = tiles_m * tiles_n;
+    int grid = device_cus() * per_cu;
+    if (c.persistent == 0 || grid > T_total)
+        grid = T_total;
+    hipLaunchKernelGGL((gemm_kernel<ROUTE, BM, BN, WM, WN, STAGES>), dim3(grid), dim3(T::kThreads), 0, a.stream,
+                       (const uint8_t*)a.A, a.a_scale, (const uint8_t*)a.B, a.b_scale, (uint16_t*)a.C, a.M, a.N,
+                       a.K, tiles_m, tiles_n, c.group_m > 0 ? c.group_m : 1, c.xcd_remap);
+    return hipGetLastError();
+}
+
+// Instantiated shapes: {BM, BN, WM, WN, STAGES}. Index = GemmConfig::variant.
+#define FP8BS_VARIANTS(X)        \
+    X(0, 128, 128, 2, 2, 3)      \
+    X(1, 256, 256, 4, 2, 2)      \
+    X(2, 256, 256, 2, 4, 2)      \
+    X(3, 128, 256, 2, 2, 3)      \
+    X(4, 256, 128, 2, 2, 3)      \
+    X(5, 128, 256, 2, 4, 3)      \
+    X(6, 256, 128, 4, 2, 3)      \
+    X(7, 128, 64, 2, 1, 3)       \
+    X(8, 256, 128, 4, 2, 2)      \
+    X(9, 128, 128, 2, 2, 4)
+
+const VariantInfo* variant_info(int v)
+{
+    static const VariantInfo table[] = {
+#define X(id, bm, bn, wm, wn, st) {bm, bn, wm, wn, st},
+        FP8BS_VARIANTS(X)
+#undef X
+    };
+    if (v < 0 || v >= (int)(sizeof(table) / sizeof(table[0])))
+        return nullptr;
+    return &table[v];
+}
+
+template <int BM, int BN, int WM, int WN, int ST>
+static constexpr bool mx_fits()
+{
+    return (BM / WM) % 64 == 0 && (BN / WN) % 64 == 0 && ST * (BM * 132 + BN * 132) <= kLdsCapacity;
+}
+
+template <int BM, int BN, int WM, int WN, int ST>
+static hipError_t launch_variant(int route, const GemmArgs& a, const GemmConfig& c)
+{
+    constexpr int TN = BN / WN;
+    if (route == kRouteBS) {
+        if constexpr (TN <= 128 && 128 % TN == 0)
+            return launch_tile<kRouteBS, BM, BN, WM, WN, ST>(a, c);
+        else
+            return hipErrorInvalidValue;
+    }
+    if constexpr (mx_fits<BM, BN, WM, WN, ST>())
+        return launch_tile<kRouteMX, BM, BN, WM, WN, ST>(a, c);
+    else
+        return hipErrorInvalidValue;
+}
+
+bool variant_supports(int route, int v)
+{
+    const VariantInfo* vi = variant_info(v);
+    if (!vi)
+        return false;
+    const int TM = vi->block_m / vi->waves_m, TN = vi->block_n / vi->waves_n;
+    if (route == kRouteBS)
+        return TN <= 128 && 128 % TN == 0;
+    return TM % 64 == 0 && TN % 64 == 0 && vi->stages * (vi->block_m * 132 + vi->block_n * 132) <= kLdsCapacity;
+}
+
+hipError_t launch_gemm(int route, const GemmArgs& a, const GemmConfig& c)
+{
+    switch (c.variant) {
+#define X(id, bm, bn, wm, wn, st) \
+    case id:                      \
+        return launch_variant<bm, bn, wm, wn, st>(route, a, c);
+        FP8BS_VARIANTS(X)
+#undef X
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace fp8bs

@@ -6,29 +6,35 @@
 
 namespace fp8bs {
 
-struct BsArgs {
-    const void* A;
-    const float* a_scale;  // [K/128, M]
-    const void* B;         // prepared weights
-    const float* b_scale;  // [N/128, K/128]
-    void* C;
+enum { kRouteBS = 0, kRouteMX = 1 };
+
+struct GemmArgs {
+    const void* A;        // [M, K] e4m3
+    const void* a_scale;  // BS: fp32 [K/128, M]; MX: packed ue8m0 dwords
+    const void* B;        // prepared weights
+    const void* b_scale;  // BS: fp32 [N/128, K/128]; MX: packed ue8m0 dwords
+    void* C;              // [M, N] bf16
     int M, N, K;
     hipStream_t stream;
 };
 
-struct MxArgs {
-    const void* A;
-    const void* a_packed;
-    const void* B;         // prepared weights
-    const void* b_packed;
-    void* C;
-    int M, N, K;
-    hipStream_t stream;
+// One instantiated kernel shape: BM x BN output tile, WM x WN waves, STAGES LDS buffers.
+struct VariantInfo {
+    int block_m, block_n, waves_m, waves_n, stages;
 };
 
-hipError_t launch_bs(const BsArgs& a);
-hipError_t launch_mx(const MxArgs& a);
+struct GemmConfig {
+    int variant;     // index into the instantiated shapes (variant_info)
+    int group_m;     // tile rows walked together by consecutive tiles
+    int xcd_remap;   // give each XCD a contiguous range of the tile order
+    int persistent;  // 1: one workgroup per CU slot looping over tiles; 0: one per tile
+};
+
+const VariantInfo* variant_info(int v);
+int device_cus();
+bool variant_supports(int route, int v);
+hipError_t launch_gemm(int route, const GemmArgs& a, const GemmConfig& c);
 hipError_t launch_prep_weights(const void* B, void* B_prep, int N, int K, hipStream_t stream);
-hipError_t launch_pack_scales(const void* e8m0, void* packed, int rows, int K, hipStream_t stream);
+hipError_t launch_pack_scales(const void* e8m0, void* packed, int rows, int K, int permute, hipStream_t stream);
 
 }  // namespace fp8bs

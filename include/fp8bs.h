@@ -113,6 +113,42 @@ int fp8mx_pack_a_scale(const void *a_e8m0, void *a_scale_packed, int M, int K, h
 int fp8mx_gemm(const void *A, const void *a_scale_packed, const void *B_prep,
                const void *b_scale_packed, void *C, int M, int N, int K, hipStream_t stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Kernel configuration (introspection and ablation). The plain entry points pick a
+ * configuration from (M, N, K) alone (page "Flydsl Fp8 Blockscale Gemm", Per-shape recipes:
+ * selection by shape, never by layer name); the *_with_config entry points run an explicit one
+ * so that tile shapes and the XCD mapping can be measured one against another (same page,
+ * Bottleneck diagnosis: ablation is the ground truth).
+ * ------------------------------------------------------------------------------------------ */
+
+enum { FP8BS_ROUTE_BS = 0, FP8BS_ROUTE_MX = 1 };
+
+typedef struct {
+    int block_m;     /* rows of C per workgroup tile                                           */
+    int block_n;     /* columns of C per workgroup tile (N must be a multiple)                 */
+    int waves_m;     /* wave grid inside the workgroup: waves_m x waves_n waves of 64 lanes    */
+    int waves_n;
+    int stages;      /* LDS buffers in the load ring (prefetch depth stages-1 K blocks)        */
+    int group_m;     /* tile rows walked together by consecutive tiles (>= 1)                  */
+    int xcd_remap;   /* 1: hand each of the 8 XCDs a contiguous range of tiles (L2 locality)   */
+    int persistent;  /* 1: one workgroup per CU slot walks several tiles; 0: one per tile      */
+} fp8bs_config;
+
+/* The configuration fp8bs_gemm (route FP8BS_ROUTE_BS) or fp8mx_gemm (FP8BS_ROUTE_MX) uses for
+ * this shape. Host-only and pure; returns FP8BS_E_SHAPE for shapes the route rejects. */
+int fp8bs_select_config(int route, int M, int N, int K, fp8bs_config *out);
+
+/* fp8bs_gemm / fp8mx_gemm with an explicit configuration. The (block_m, block_n, waves_m,
+ * waves_n, stages) tuple must be one the library instantiates and valid for the route, and N
+ * must be a multiple of block_n; otherwise FP8BS_E_CONFIG and nothing is launched. Every
+ * configuration performs the same per-element arithmetic in the same order, so results are
+ * bitwise identical to the plain entry point's. */
+int fp8bs_gemm_with_config(const void *A, const float *a_scale, const void *B_prep, const float *b_scale,
+                           void *C, int M, int N, int K, const fp8bs_config *config, hipStream_t stream);
+int fp8mx_gemm_with_config(const void *A, const void *a_scale_packed, const void *B_prep,
+                           const void *b_scale_packed, void *C, int M, int N, int K,
+                           const fp8bs_config *config, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

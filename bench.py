@@ -4,20 +4,32 @@ One step = one fp8bs_gemm launch on the narrow-N, deep-K workload (M=4096, N=204
 route BS: fp32 per-1x128 activation scales, fp32 per-128x128 weight scales, bf16 out), with
 every input already resident in HBM. Prints ONE JSON line on stdout:
 
-  value      -- TFLOP/s (2*M*N*K per step / wall time per step) of that workload
-  roofline   -- the GEMM kernel's achieved TFLOP/s from HIP events on its own stream,
-                against the dense fp8 matrix-core peak (5.0 PFLOP/s); traffic from the
-                committed rocprofv3 counter summary when it matches the current kernel source
-  per_shape  -- the same measurement for all five workloads (tiny, narrow-N, K-light, wide-N,
-                mxfp8) with % of peak and algorithmic HBM GB/s
-  cpu_baseline -- the CPU oracle (fp64, OpenMP) on a bounded sample of rows of the workload
-  parity     -- sampled rows/columns of the timed output against the oracle
+  value        -- TFLOP/s (2*M*N*K per step / wall time per step) of that workload
+  roofline     -- the GEMM kernel's achieved TFLOP/s from HIP events on its own stream,
+                  against the dense fp8 matrix-core peak (5.0 PFLOP/s); traffic from the
+                  committed rocprofv3 counter record when it matches the current kernel source
+  mfma_ceiling -- the matrix core's sustained rate on this workload's own operand bytes with
+                  no memory traffic (the gfx950 matrix core slows down when operand bits
+                  change between instructions; this is the reachable ceiling for this data)
+  per_shape    -- steady-state time of all five workloads (tiny, narrow-N, K-light, wide-N,
+                  mxfp8), TFLOP/s, % of peak, algorithmic HBM GB/s
+  cpu_baseline -- the CPU oracle (fp64, OpenMP) on a bounded sample of output rows
+  parity       -- sampled rows/columns of the timed output against the oracle
+
+The GPU raises its clock over the first ~20 ms of sustained work, so every measurement is
+preceded by a warmup of that order (the default --warmup covers it for the main workload).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only NAME]
+       python bench.py --profile NAME [--steps K]       (for rocprofv3 runs; also runs a copy
+                                                          of known size for counter scaling)
+       python bench.py --ingest-counters DIR            (rocprofv3 FETCH_SIZE / WRITE_SIZE
+                                                          csv dirs -> profiles/traffic.json)
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -31,7 +43,9 @@ PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 matrix-core peak (published), TFL
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E bandwidth (published), GB/s
 METRIC = "fp8 blockscale GEMM TFLOP/s and % of MI355X dense fp8 MFMA peak, per shape"
 MAIN = "narrow_n"
-KERNEL_SOURCES = ["gemm.hip", "device.hpp"]
+KERNEL_SOURCES = ["gemm.hip", "device.hpp", "prep.hip"]
+COPY_BYTES = 256 << 20      # calibration copy for the byte counters
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def log(*a):
@@ -58,12 +72,13 @@ def algorithmic_bytes(route: str, M: int, N: int, K: int) -> int:
 class Case:
     """Device-resident operands of one workload plus a launch closure on a given stream."""
 
-    def __init__(self, name: str, cfg: dict, seed: int, stream):
+    def __init__(self, name: str, seed: int, stream):
         import torch
 
         import fp8_block_scaled_e4m3_amd as fb
         import workload
 
+        cfg = workload.CONFIGS[name]
         self.name, self.route = name, cfg["route"]
         self.M, self.N, self.K = cfg["M"], cfg["N"], cfg["K"]
         dev = torch.device("cuda:0")
@@ -87,13 +102,16 @@ class Case:
         log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s")
         fn = fb.fp8bs_gemm if self.route == "bs" else fb.fp8mx_gemm
         self.launch = lambda: fn(self.A, self.sa, self.B, self.sb, self.C, stream)
+        self.config = fb.fp8bs_select_config(fb.ROUTE_BS if self.route == "bs" else fb.ROUTE_MX,
+                                             self.M, self.N, self.K).as_dict()
 
     @property
     def flops(self) -> int:
         return 2 * self.M * self.N * self.K
 
     def time_launches(self, steps: int, warmup: int, stream):
-        """(wall seconds per launch, event seconds per launch) over `steps` launches."""
+        """(wall seconds per launch, event seconds per launch) over exactly `steps` launches
+        after `warmup` untimed ones; synchronised on both sides of the timed region."""
         import torch
         for _ in range(warmup):
             self.launch()
@@ -110,18 +128,57 @@ class Case:
         ev = e0.elapsed_time(e1) / 1e3 / steps
         return wall, ev
 
+    def steady_state(self, stream, warm_s: float = 0.06, time_s: float = 0.06):
+        """Warm up for warm_s seconds of launches, then time about time_s seconds of them."""
+        import torch
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < warm_s or n < 5:
+            self.launch()
+            n += 1
+            if n % 16 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        per = max((time.perf_counter() - t0) / n, 1e-6)
+        steps = int(min(2000, max(50, time_s / per)))
+        return self.time_launches(steps, 0, stream) + (steps,)
+
     def free(self):
         for k in ("A", "sa", "B", "sb", "C"):
             setattr(self, k, None)
 
 
+def mfma_ceiling(case: Case, stream, iters: int = 512) -> dict:
+    """Sustained matrix-core rate on the case's own operand bytes (no memory traffic)."""
+    import torch
+
+    import fp8_block_scaled_e4m3_amd as fb
+    sink = torch.empty(256 * 8 * 4, dtype=torch.float32, device=case.A.device)
+    for _ in range(20):  # warm (clock ramp)
+        fb.fp8bs_mfma_ceiling(case.A, case.B, case.N, iters, sink, stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    reps = 10
+    flops = 0
+    for _ in range(reps):
+        flops += fb.fp8bs_mfma_ceiling(case.A, case.B, case.N, iters, sink, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    tflops = flops / (e0.elapsed_time(e1) / 1e3) / 1e12
+    return {"tflops": round(tflops, 1), "frac_of_peak": round(tflops / PEAK_FP8_TFLOPS, 4),
+            "operands": f"{case.name} A and prepared B fragments", "kernel": "mfma_ceiling_kernel"}
+
+
 def sampled_parity(case: Case, nrows: int = 16, ncols: int = 16) -> dict:
     import numpy as np
+    import torch
 
     import oracle
     import workload
     o = oracle.load()
-    got = case.C.view(__import__("torch").int16).cpu().numpy().view(np.uint16)
+    got = case.C.view(torch.int16).cpu().numpy().view(np.uint16)
     rows = workload.sample_indices(case.M, nrows, 100)
     cols = workload.sample_indices(case.N, ncols, 101)
     h = case.host
@@ -141,7 +198,8 @@ def sampled_parity(case: Case, nrows: int = 16, ncols: int = 16) -> dict:
 
 
 def cpu_baseline(case: Case, target_s: float = 12.0) -> dict:
-    """The oracle as it stands, on a bounded sample of whole output rows of the workload."""
+    """The oracle as it stands, on a bounded sample of whole output rows of the workload
+    (all M rows when they take less than target_s)."""
     import numpy as np
 
     import oracle
@@ -167,12 +225,11 @@ def cpu_baseline(case: Case, target_s: float = 12.0) -> dict:
 
 
 def committed_traffic(workload_name: str):
-    """HBM traffic per launch from the committed counter summary, if it was taken on the
-    current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
+    """HBM bytes per launch from the committed counter record, if it was taken on the current
+    kernel source; otherwise None."""
+    if not os.path.exists(TRAFFIC_RECORD):
         return None
-    with open(path) as f:
+    with open(TRAFFIC_RECORD) as f:
         rec = json.load(f)
     entry = rec.get(workload_name)
     if not entry or entry.get("kernel_source_sha256") != kernel_source_hash():
@@ -180,15 +237,87 @@ def committed_traffic(workload_name: str):
     return entry.get("traffic_bytes")
 
 
+# ---- rocprofv3 helpers -----------------------------------------------------------------------
+
+def profile_mode(name: str, steps: int, warmup: int) -> int:
+    """Launch one workload `steps` times after `warmup`, then one device copy of COPY_BYTES
+    (the byte counters of that copy calibrate FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        case = Case(name, 0, stream)
+        wall, ev = case.time_launches(steps, warmup, stream)
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+    print(json.dumps({"profile": name, "steps": steps, "warmup": warmup, "avg_launch_us": round(ev * 1e6, 2),
+                      "copy_bytes": COPY_BYTES, "config": case.config}), flush=True)
+    return 0
+
+
+def ingest_counters(dirs: list[str]) -> int:
+    """Read rocprofv3 counter_collection.csv files (one FETCH_SIZE and one WRITE_SIZE run of
+    `bench.py --profile NAME`), scale each counter by what it read for the calibration copy of
+    known size, and record per-launch HBM traffic in profiles/traffic.json."""
+    per_counter = {}
+    workload_name = None
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                rows = list(csv.DictReader(f))
+            for r in rows:
+                name = r["Counter_Name"]
+                if name not in ("FETCH_SIZE", "WRITE_SIZE"):
+                    continue
+                kern = r["Kernel_Name"]
+                val = float(r["Counter_Value"]) * 1024.0  # counters are in KiB
+                per_counter.setdefault(name, {}).setdefault(kern, []).append(val)
+        meta = os.path.join(d, "profile.json")
+        if os.path.exists(meta):
+            workload_name = json.load(open(meta))["profile"]
+    if not workload_name:
+        print("no profile.json (the --profile output) found next to the counter csv", file=sys.stderr)
+        return 2
+    out = {}
+    for counter, kernels in per_counter.items():
+        gemm = [v for k, vals in kernels.items() if "gemm_kernel" in k for v in vals]
+        copy = [v for k, vals in kernels.items() if "copyBuffer" in k or "elementwise" in k.lower() for v in vals]
+        copy = [max(copy)] if copy else []
+        if not gemm or not copy:
+            continue
+        factor = COPY_BYTES / copy[0]
+        gemm_bytes = sorted(gemm)[len(gemm) // 2] * factor  # median over launches
+        out[counter] = {"raw_bytes_per_launch": sorted(gemm)[len(gemm) // 2], "copy_raw_bytes": copy[0],
+                        "scale": factor, "bytes_per_launch": gemm_bytes}
+    if "FETCH_SIZE" not in out or "WRITE_SIZE" not in out:
+        print(f"missing counters: {sorted(out)}", file=sys.stderr)
+        return 2
+    rec = json.load(open(TRAFFIC_RECORD)) if os.path.exists(TRAFFIC_RECORD) else {}
+    rec[workload_name] = {"kernel_source_sha256": kernel_source_hash(),
+                          "traffic_bytes": round(out["FETCH_SIZE"]["bytes_per_launch"] +
+                                                 out["WRITE_SIZE"]["bytes_per_launch"]),
+                          "counters": out}
+    with open(TRAFFIC_RECORD, "w") as f:
+        json.dump(rec, f, indent=1, sort_keys=True)
+    print(json.dumps(rec[workload_name]))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only", default=None, help="time only this workload (plus the main one)")
-    ap.add_argument("--shape-steps", type=int, default=30)
+    ap.add_argument("--profile", default=None, help="rocprofv3 driver mode for one workload")
+    ap.add_argument("--ingest-counters", nargs="+", default=None)
     args = ap.parse_args()
+    if args.ingest_counters:
+        return ingest_counters(args.ingest_counters)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library is a single-GPU kernel and no "
               "multi-GPU path exists (run with --gpus 1).", file=sys.stderr)
@@ -200,34 +329,39 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU (cuda:0)", file=sys.stderr)
         return 2
+    if args.profile:
+        return profile_mode(args.profile, args.steps, args.warmup)
     props = torch.cuda.get_device_properties(0)
     stream = torch.cuda.Stream()
     per_shape = {}
-    main_row = None
     names = [MAIN] + [n for n in workload.CONFIGS if n != MAIN]
     if args.only:
         names = [MAIN] + ([args.only] if args.only != MAIN else [])
+    main_row = None
     with torch.cuda.stream(stream):
         for name in names:
-            cfg = workload.CONFIGS[name]
-            case = Case(name, cfg, 0, stream)
-            steps = args.steps if name == MAIN else args.shape_steps
-            warm = args.warmup if name == MAIN else max(3, args.warmup // 2)
-            wall, ev = case.time_launches(steps, warm, stream)
+            case = Case(name, 0, stream)
+            if name == MAIN:
+                wall, ev = case.time_launches(args.steps, args.warmup, stream)
+                steps = args.steps
+            else:
+                wall, ev, steps = case.steady_state(stream)
             tflops = case.flops / ev / 1e12
             nbytes = algorithmic_bytes(case.route, case.M, case.N, case.K)
             row = dict(M=case.M, N=case.N, K=case.K, route=case.route, us=round(ev * 1e6, 2),
                        tflops=round(tflops, 1), pct_peak=round(100 * tflops / PEAK_FP8_TFLOPS, 2),
-                       hbm_gbs_algorithmic=round(nbytes / ev / 1e9, 1))
+                       hbm_gbs_algorithmic=round(nbytes / ev / 1e9, 1), timed_launches=steps,
+                       config=case.config)
             log(f"[bench] {name}: {row}")
             if name == MAIN:
                 row["parity"] = sampled_parity(case)
                 log(f"[bench] parity {row['parity']}")
-                main_row = dict(wall=wall, ev=ev, case=case, nbytes=nbytes, steps=steps, warmup=warm)
+                ceiling = mfma_ceiling(case, stream)
+                log(f"[bench] mfma ceiling {ceiling}")
                 baseline = None if args.no_cpu else cpu_baseline(case)
                 if baseline:
                     log(f"[bench] cpu baseline {baseline}")
-                main_row["baseline"] = baseline
+                main_row = dict(wall=wall, ev=ev, case=case, nbytes=nbytes, baseline=baseline, ceiling=ceiling)
             else:
                 case.free()
                 del case
@@ -242,8 +376,8 @@ def main() -> int:
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": main_row["steps"],
-        "warmup": main_row["warmup"],
+        "steps": args.steps,
+        "warmup": args.warmup,
         "ms_per_step": round(main_row["wall"] * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -257,7 +391,8 @@ def main() -> int:
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
                      "traffic": committed_traffic(MAIN),
                      "kernel": "gemm_kernel (route BS)", "avg_launch_us": round(main_row["ev"] * 1e6, 2),
-                     "flop_per_launch": case.flops},
+                     "flop_per_launch": case.flops, "algorithmic_bytes": main_row["nbytes"]},
+        "mfma_ceiling": main_row["ceiling"],
         "cpu_baseline": main_row["baseline"],
         "per_shape": per_shape,
         "device": {"name": props.name, "cus": props.multi_processor_count,

@@ -25,6 +25,7 @@ __all__ = [
     "fp8mx_packed_scale_bytes", "fp8mx_pack_a_scale", "fp8mx_prep_weights", "fp8mx_gemm",
     "prep_weights", "mx_prep_weights", "mx_pack_a_scale",
     "Config", "ROUTE_BS", "ROUTE_MX", "fp8bs_select_config", "fp8bs_gemm_with_config", "fp8mx_gemm_with_config",
+    "fp8bs_mfma_ceiling",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -45,6 +46,7 @@ SIGNATURES = {
     "fp8bs_select_config": (_int, [_int, _int, _int, _int, _vp]),
     "fp8bs_gemm_with_config": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp, _vp]),
     "fp8mx_gemm_with_config": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp, _vp]),
+    "fp8bs_mfma_ceiling": (_int, [_vp, _vp, _int, _int, _int, _int, _vp, _int, _vp, _vp]),
 }
 
 ROUTE_BS, ROUTE_MX = 0, 1
@@ -185,6 +187,17 @@ def fp8mx_gemm_with_config(A, a_scale_packed, B_prep, b_scale_packed, C, config:
            lib.fp8mx_gemm_with_config(_ptr(A), _ptr(a_scale_packed), _ptr(B_prep), _ptr(b_scale_packed), _ptr(C),
                                       M, N, K, ctypes.byref(config), _stream(stream)))
     return C
+
+
+def fp8bs_mfma_ceiling(A: torch.Tensor, B_prep: torch.Tensor, N: int, iters: int, sink: torch.Tensor,
+                       stream=None) -> int:
+    """Launch the matrix-core ceiling probe on A [M,K] and prepared weights of N rows; returns the
+    FLOP count of the launch (time it with events on the stream)."""
+    M, K = A.shape
+    flops = ctypes.c_longlong(0)
+    _check("fp8bs_mfma_ceiling", lib.fp8bs_mfma_ceiling(_ptr(A), _ptr(B_prep), M, N, K, iters, _ptr(sink),
+                                                        sink.numel(), ctypes.byref(flops), _stream(stream)))
+    return flops.value
 
 
 # ---- allocation helpers (torch owns the memory; the library never allocates) ----------------

@@ -266,4 +266,16 @@ int fp8mx_gemm_with_config(const void* A, const void* a_scale_packed, const void
     return run(fp8bs::kRouteMX, A, a_scale_packed, B_prep, b_scale_packed, C, M, N, K, config, stream);
 }
 
+int fp8bs_mfma_ceiling(const void* A, const void* B_prep, int M, int N, int K, int iters, float* sink, int sink_len,
+                       long long* flops, hipStream_t stream)
+{
+    if (M < 64 || N < 64 || K < 128 || K % 128 != 0 || iters < 1 || sink_len < 8 || !fits_offsets(M, N, K))
+        return FP8BS_E_SHAPE;
+    if (!A || !B_prep || !sink)
+        return FP8BS_E_NULL;
+    if (!aligned(A, 16) || !aligned(B_prep, 16) || !aligned(sink, 4))
+        return FP8BS_E_ALIGN;
+    return hip_status(fp8bs::launch_mfma_ceiling(A, B_prep, M, N, K, iters, sink, sink_len, flops, stream));
+}
+
 }  // extern "C"

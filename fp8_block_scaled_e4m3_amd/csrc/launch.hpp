@@ -34,6 +34,8 @@ const VariantInfo* variant_info(int v);
 int device_cus();
 bool variant_supports(int route, int v);
 hipError_t launch_gemm(int route, const GemmArgs& a, const GemmConfig& c);
+hipError_t launch_mfma_ceiling(const void* A, const void* B_prep, int M, int N, int K, int iters, float* sink,
+                               int sink_len, long long* flops, hipStream_t stream);
 hipError_t launch_prep_weights(const void* B, void* B_prep, int N, int K, hipStream_t stream);
 hipError_t launch_pack_scales(const void* e8m0, void* packed, int rows, int K, int permute, hipStream_t stream);
 

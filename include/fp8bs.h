@@ -149,6 +149,19 @@ int fp8mx_gemm_with_config(const void *A, const void *a_scale_packed, const void
                            const void *b_scale_packed, void *C, int M, int N, int K,
                            const fp8bs_config *config, hipStream_t stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Diagnostic (not part of the GEMM): the matrix core's sustained fp8 rate on the caller's own
+ * operand bytes, with no memory traffic in the timed loop. On gfx950 the matrix-core rate
+ * depends on how much the operand bits change between instructions, so this is the ceiling
+ * the GEMM can reach on this data (page "Flydsl Fp8 Blockscale Gemm", Bottleneck diagnosis:
+ * an identical-MFMA-work instrument). One workgroup of 8 waves per CU; each wave runs
+ * iters x 16 instructions on fragments read from A [M,K] and B_prep (fp8bs_prep_weights).
+ * sink: device buffer of sink_len floats (>= 8 per workgroup launched; at most one
+ * workgroup per CU is launched and fewer if sink_len is short); flops (host, may be NULL)
+ * receives the FLOP count of the launch. Time it with events on `stream`. */
+int fp8bs_mfma_ceiling(const void *A, const void *B_prep, int M, int N, int K, int iters, float *sink,
+                       int sink_len, long long *flops, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -72,16 +72,26 @@ fp8bs_config select(int route, int M, int N, int K)
 {
     (void)K;
     const int kCUs = 256;
+    const int group_m = 4;
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * (N / bn); };
+    // The XCD remap keeps the tiles that one XCD runs at the same time next to each other,
+    // which pays while a band of group_m tile rows holds at most about two waves of resident
+    // workgroups. On wider outputs the plain round-robin order runs every XCD on the same band
+    // at once, so each weight panel is reused by all the tile rows that need it while it is
+    // still cached (measured on the 4096 x 65536 x 1536 shape: about 8% faster).
+    auto cfg = [&](int variant, int block_n) {
+        const int xcd = group_m * (N / block_n) <= 2 * kCUs ? 1 : 0;
+        return make_config(variant, group_m, xcd, 1);
+    };
     if (route == fp8bs::kRouteMX && N % 128 != 0)
-        return make_config(7, 4, 1, 1);
+        return cfg(7, 64);
     if (N % 256 == 0 && tiles(256, 256) >= 2 * kCUs)
-        return make_config(2, 4, 1, 1);
+        return cfg(2, 256);
     if (tiles(256, 128) >= kCUs)
-        return make_config(6, 4, 1, 1);
+        return cfg(6, 128);
     if (N % 256 == 0 && tiles(128, 256) >= kCUs)
-        return make_config(5, 4, 1, 1);
-    return make_config(0, 4, 1, 1);
+        return cfg(5, 256);
+    return cfg(0, 128);
 }
 
 int check_config(int route, const fp8bs_config* c, int N, fp8bs::GemmConfig* out)

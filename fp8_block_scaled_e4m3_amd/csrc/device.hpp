@@ -44,13 +44,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// LDS tile of R rows x 128 bytes, stored row-major with the 16-byte chunks of each row
-// XOR-swizzled by (row & 7) so that the sixteen lanes reading the same chunk of sixteen
-// consecutive rows spread over all banks.
-__device__ __forceinline__ uint32_t lds_tile_offset(uint32_t row, uint32_t chunk) {
-    return row * 128u + ((chunk ^ (row & 7u)) << 4);
-}
-
 // Row order of the prepared weight buffer inside each 64-row window: prepared row
 // rho = 16j + 4a + r (sub-tile j, output lane group a, register r of the swap-AB result) holds
 // weight row 32*(j/2) + 8a + 4*(j%2) + r. With this order the result registers of sub-tiles

@@ -3,9 +3,9 @@
 // Route BS (page "Flydsl Fp8 Blockscale Gemm", Mechanism A): fp32 block scales cannot be
 // expressed by the matrix core's power-of-two scale operands, so each 128-wide K block of a
 // 16x16 output tile is one UNSCALED v_mfma_f32_16x16x128_f8f6f4 into a fresh fp32 partial
-// (four VGPRs), immediately "promoted": acc += partial * (a_s[m,kb] * b_s[n/128,kb]). The
-// promote is 4 fp32 FMAs per instruction, interleaved by the compiler with the following
-// matrix instructions so the vector ALU works while the matrix core runs.
+// (four VGPRs), then "promoted": acc += partial * (a_s[m,kb] * b_s[n/128,kb]). The promote
+// is 4 fp32 FMAs per instruction, issued two matrix instructions after the one it reads, so
+// the vector ALU works while the matrix core runs and neither waits on the other.
 //
 // Route MX (page "aiter PR #6370", "Why it is faster"): the 1x32 ue8m0 scales ride in the
 // scale operands of v_mfma_scale_f32_16x16x128_f8f6f4, accumulating straight into acc.
@@ -17,12 +17,19 @@
 //    tile starts on data that is already in LDS and a finished tile's C stores drain while
 //    the next tile computes.
 //  * Operands move global -> LDS with buffer_load_dwordx4 ... lds (no staging registers; the
-//    K advance is a scalar offset) into a ring of STAGES LDS buffers, one barrier per step.
-//    The block scales of the step travel in the same buffer (buffer_load_dword ... lds), so
-//    every wave issues the same number of loads per step and a single vmcnt wait covers them.
+//    K advance is a scalar offset) into a ring of STAGES LDS buffers. The block scales of the
+//    step travel in the same buffer (buffer_load_dword ... lds), so every wave issues the same
+//    number of loads per step and a single vmcnt wait covers them. The loads go out one per
+//    matrix instruction: issued back to back they stall the issuing wave in the texture path
+//    for several hundred cycles each step.
 //  * Each wave computes a TM x TN sub-tile with the weights as the first matrix operand
 //    (swap-AB), so every lane owns four consecutive columns of one output row and stores
-//    8 contiguous bytes (page "aiter PR #6370", "Why it is faster", first bullet).
+//    8 contiguous bytes (page "aiter PR #6370", "Why it is faster", first bullet). Of the two
+//    operands the one with fewer fragments per wave is held in registers for the whole step
+//    and the other streams through a two-deep register ring.
+//  * One barrier per step, placed after the last matrix instruction of the step is issued:
+//    the wave then reads the first fragments of the next step while its last instructions
+//    and the promotes still run.
 //  * Tiles are handed out so that the workgroups running at the same time on one XCD (each
 //    XCD has its own L2) work on neighbouring tiles (page "Flydsl Fp8 Blockscale Gemm",
 //    Mechanism B: XCD-aware rasterisation).
@@ -75,12 +82,24 @@ struct Tile {
     static_assert(kLoadsPerStep * (STAGES - 1) <= 63, "vmcnt range");
 };
 
-// s_waitcnt with only a vmcnt limit (expcnt and lgkmcnt left unconstrained).
+// s_waitcnt for vmcnt <= N and lgkmcnt == 0 (expcnt left unconstrained).
 template <int N>
-__device__ __forceinline__ void wait_vmcnt()
+__device__ __forceinline__ void wait_vmcnt_lgkm()
 {
     static_assert(N >= 0 && N <= 63, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Tile u of the persistent order -> output tile (tm, tn). Workgroup ids are dispatched
@@ -102,31 +121,6 @@ __device__ __forceinline__ void tile_of(int u, int tiles_m, int tiles_n, int gro
     const int r = t - g * per_group;
     tm = first_m + r % gm;
     tn = r / gm;
-}
-
-// Route MX inner block: acc[I][J] += scaled(B_J, A_I) for all sub-tiles, with the op_sel
-// byte of each packed scale dword chosen at compile time (sub-tile index mod 4).
-template <int I, int J, int SI, int SJ, int GA, int GB>
-__device__ __forceinline__ void mx_rows(v4f (&acc)[SI][SJ], const v8i (&af)[SI], const v8i& bf,
-                                        const int (&sa)[GA], const int (&sb)[GB])
-{
-    if constexpr (I < SI) {
-        // weights first: the weight scale byte of sub-tile J, the activation byte of sub-tile I
-        acc[I][J] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af[I], acc[I][J], kFmtE4M3, kFmtE4M3,
-                                                                     J & 3, sb[J / 4], I & 3, sa[I / 4]);
-        mx_rows<I + 1, J>(acc, af, bf, sa, sb);
-    }
-}
-
-template <int J, int SI, int SJ, int GA, int GB, typename Frag>
-__device__ __forceinline__ void mx_cols(v4f (&acc)[SI][SJ], const v8i (&af)[SI], const int (&sa)[GA],
-                                        const int (&sb)[GB], const uint8_t* sB, Frag& frag)
-{
-    if constexpr (J < SJ) {
-        const v8i bf = frag(sB + J * 16 * 128);
-        mx_rows<0, J>(acc, af, bf, sa, sb);
-        mx_cols<J + 1>(acc, af, sa, sb, sB, frag);
-    }
 }
 
 template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES>
@@ -208,33 +202,51 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
         }
         load_tile = i;
     };
-    auto issue_loads = [&](lds_u8* st, int step) {
-        const int i = step / KB;
-        const int kb = step - i * KB;
-        if (i != load_tile)
-            setup_loads(i);
-        const int koff = kb * 128;
-        lds_u8* sA = st;
-        lds_u8* sB = st + T::kABytes;
-        lds_u8* sS = st + T::kABytes + T::kBBytes;
-#pragma unroll
-        for (int g = 0; g < T::kLoadsA; ++g)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(sA + (wave * T::kLoadsA + g) * 1024), 16,
+    // Loads are issued in stream order, one group (kLoadsPerStep loads per wave) per step;
+    // (ld_tile, ld_kb) is the next step to load. Past the end of the stream a group is still
+    // issued, as an in-bounds re-read of the last loaded tile's first K block into a stage that
+    // no later step reads, so that every step issues exactly one group and every vmcnt wait is
+    // a compile-time constant.
+    int ld_tile = 0, ld_kb = 0;
+    int ld_kbv = 0;  // K block of the planned group
+    auto plan_loads = [&](bool real) {
+        int kb = 0;
+        if (real) {
+            if (ld_tile != load_tile)
+                setup_loads(ld_tile);
+            kb = ld_kb;
+            if (++ld_kb == KB) {
+                ld_kb = 0;
+                ++ld_tile;
+            }
+        }
+        ld_kbv = kb;
+    };
+    // Load g of the planned group into stage st: A rows, then B rows, then block scales.
+    auto issue_load = [&](auto G, lds_u8* st) {
+        constexpr int g = decltype(G)::value;
+        const int koff = ld_kbv * 128;
+        if constexpr (g < T::kLoadsA) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(st + (wave * T::kLoadsA + g) * 1024), 16,
                                                      (int)voffA[g], koff, 0, 0);
-#pragma unroll
-        for (int g = 0; g < T::kLoadsB; ++g)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void*)(sB + (wave * T::kLoadsB + g) * 1024), 16,
-                                                     (int)voffB[g], koff, 0, 0);
-#pragma unroll
-        for (int g = 0; g < T::kLoadsS; ++g) {
-            const int u = min(wave * T::kLoadsS + g, T::kScaleLoads - 1);  // uniform
-            const int soff = kb * (int)kstrS[g];
+        } else if constexpr (g < T::kLoadsA + T::kLoadsB) {
+            constexpr int gb = g - T::kLoadsA;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void*)(st + T::kABytes + (wave * T::kLoadsB + gb) * 1024),
+                                                     16, (int)voffB[gb], koff, 0, 0);
+        } else {
+            constexpr int gs = g - T::kLoadsA - T::kLoadsB;
+            lds_u8* sS = st + T::kABytes + T::kBBytes;
+            const int u = min(wave * T::kLoadsS + gs, T::kScaleLoads - 1);  // uniform
+            const int soff = __builtin_amdgcn_readfirstlane(ld_kbv * (int)kstrS[gs]);  // uniform
             if (u < T::kScaleLoadsA)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsSA, (lds_void*)(sS + u * 256), 4, (int)voffS[g], soff, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsSA, (lds_void*)(sS + u * 256), 4, (int)voffS[gs], soff, 0, 0);
             else
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rsSB, (lds_void*)(sS + T::kSABytes + (u - T::kScaleLoadsA) * 256),
-                                                         4, (int)voffS[g], soff, 0, 0);
+                                                         4, (int)voffS[gs], soff, 0, 0);
         }
+    };
+    auto issue_group = [&](lds_u8* st) {
+        static_for<T::kLoadsPerStep>([&](auto G) { issue_load(G, st); });
     };
 
     v4f acc[T::SI][T::SJ];
@@ -252,6 +264,16 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     auto frag = [&](const uint8_t* base) -> v8i {
         const v4i lo = *(const v4i*)(base + c_lo);
         const v4i hi = *(const v4i*)(base + c_hi);
+        return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    };
+    // The same read, kept in place: the optimiser may not move it above the preceding
+    // instructions (it would otherwise hoist every streamed read of a step to its start and
+    // hold them all in registers).
+    auto frag_here = [&](const uint8_t* base) -> v8i {
+        uint32_t lo_off = c_lo, hi_off = c_hi;
+        asm volatile("" : "+v"(lo_off), "+v"(hi_off));
+        const v4i lo = *(const v4i*)(base + lo_off);
+        const v4i hi = *(const v4i*)(base + hi_off);
         return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     };
 
@@ -287,83 +309,172 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
         }
     };
 
-    // ---- compute one step from a stage ----------------------------------------------------
-    auto compute = [&](const uint8_t* st) {
-        const uint8_t* sA = st + (wm * T::TM) * 128;
-        const uint8_t* sB = st + T::kABytes + (wn * T::TN) * 128;
+    // ---- registers of the step being computed ----------------------------------------------
+    // The operand with fewer fragments per wave is held whole; the other is streamed through a
+    // two-deep ring (fragment o+1 is read while the instructions of fragment o run).
+    constexpr bool kStreamA = T::SI >= T::SJ;
+    constexpr int NO = kStreamA ? T::SI : T::SJ;  // streamed fragments (outer loop)
+    constexpr int NH = kStreamA ? T::SJ : T::SI;  // held fragments (inner loop)
+    constexpr int GA = (T::SI + 3) / 4;           // MX: packed scale dwords per wave (one per 64 rows)
+    constexpr int GB = (T::SJ + 3) / 4;
+    v8i held[NH];
+    v8i ring[2];
+    float sa_r[ROUTE == kRouteBS ? T::SI : 1];  // BS: a_s of this lane's row in sub-tile row i
+    float sb_r = 0.f;                            // BS: b_s of the wave's weight block
+    int ia[GA];                                  // MX: packed activation scale dwords
+    int ib[GB];                                  // MX: packed weight scale dwords
+
+    auto a_base = [&](const uint8_t* st) { return st + (wm * T::TM) * 128; };
+    auto b_base = [&](const uint8_t* st) { return st + T::kABytes + (wn * T::TN) * 128; };
+    auto streamed = [&](const uint8_t* st) { return kStreamA ? a_base(st) : b_base(st); };
+    auto held_base = [&](const uint8_t* st) { return kStreamA ? b_base(st) : a_base(st); };
+
+    // The head of a step: what its first matrix instruction needs (held fragment 0 and streamed
+    // fragment 0), the scales, then the rest of the held fragments.
+    auto read_head = [&](const uint8_t* st) {
         const uint8_t* sS = st + T::kABytes + T::kBBytes;
-        v8i af[T::SI];
-#pragma unroll
-        for (int i = 0; i < T::SI; ++i)
-            af[i] = frag(sA + i * 16 * 128);
+        held[0] = frag(held_base(st));
+        ring[0] = frag(streamed(st));
         if constexpr (ROUTE == kRouteBS) {
             const float* sa = (const float*)sS + wm * T::TM + frow;
-            const float sb = ((const float*)(sS + T::kSABytes))[(wn * T::TN) >> 7];
-            float s[T::SI];
 #pragma unroll
             for (int i = 0; i < T::SI; ++i)
-                s[i] = sa[16 * i] * sb;
-#pragma unroll
-            for (int j = 0; j < T::SJ; ++j) {
-                const v8i bf = frag(sB + j * 16 * 128);
-#pragma unroll
-                for (int i = 0; i < T::SI; ++i) {
-                    const v4f p = mfma_f8(bf, af[i], v4f{0.f, 0.f, 0.f, 0.f});
-                    acc[i][j] += p * s[i];
-                }
-            }
+                sa_r[i] = sa[16 * i];
+            sb_r = ((const float*)(sS + T::kSABytes))[(wn * T::TN) >> 7];
         } else {
-            constexpr int GA = (T::SI + 3) / 4;
-            constexpr int GB = (T::SJ + 3) / 4;
-            int sa[GA];
-            int sb[GB];
 #pragma unroll
             for (int g = 0; g < GA; ++g)
-                sa[g] = ((const int*)sS)[(wm * T::TM / 64 + g) * 64 + lane];
+                ia[g] = ((const int*)sS)[(wm * T::TM / 64 + g) * 64 + lane];
 #pragma unroll
             for (int g = 0; g < GB; ++g)
-                sb[g] = ((const int*)(sS + T::kSABytes))[(wn * T::TN / 64 + g) * 64 + lane];
-            // op_sel must be a constant: walk the sub-tiles with compile-time indices.
-            mx_cols<0>(acc, af, sa, sb, sB, frag);
+                ib[g] = ((const int*)(sS + T::kSABytes))[(wn * T::TN / 64 + g) * 64 + lane];
+        }
+#pragma unroll
+        for (int h = 1; h < NH; ++h)
+            held[h] = frag(held_base(st) + h * 16 * 128);
+    };
+
+    // ---- one step's matrix work ---------------------------------------------------------------
+    // Route BS: matrix instruction t (in issue order) writes a fresh partial, and its promote
+    // (acc += partial * a_s*b_s) is issued two instructions later, once the result is ready, so
+    // the matrix core never waits on the vector ALU. Scheduling barriers keep that order.
+    // `transition` runs after the last instruction is issued and before the last two promotes.
+    v4f p[3];
+    auto rows = [&](const uint8_t* st, lds_u8* load_st, auto&& transition) {
+        const uint8_t* sO = streamed(st);
+        float srow[T::SI];
+        if constexpr (ROUTE == kRouteBS) {
+#pragma unroll
+            for (int i = 0; i < T::SI; ++i)
+                srow[i] = sa_r[i] * sb_r;
+        }
+        auto promote = [&](auto Tc) {
+            constexpr int t = decltype(Tc)::value;
+            constexpr int o = t / NH, h = t % NH;
+            constexpr int i = kStreamA ? o : h;
+            constexpr int j = kStreamA ? h : o;
+            acc[i][j] += p[t % 3] * srow[i];
+        };
+        static_for<NO>([&](auto O) {
+            constexpr int o = decltype(O)::value;
+            if constexpr (o + 1 < NO)
+                ring[(o + 1) & 1] = frag_here(sO + (o + 1) * 16 * 128);
+            static_for<NH>([&](auto H) {
+                constexpr int h = decltype(H)::value;
+                constexpr int t = o * NH + h;
+                constexpr int i = kStreamA ? o : h;
+                constexpr int j = kStreamA ? h : o;
+                const v8i& a = kStreamA ? ring[o & 1] : held[h];
+                const v8i& b = kStreamA ? held[h] : ring[o & 1];
+                if constexpr (ROUTE == kRouteBS) {
+                    p[t % 3] = mfma_f8(b, a, v4f{0.f, 0.f, 0.f, 0.f});
+                    if constexpr (t >= 2)
+                        promote(std::integral_constant<int, t - 2>{});
+                } else {
+                    // weights first: the weight scale byte of sub-tile j, the activation byte of row i
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        b, a, acc[i][j], kFmtE4M3, kFmtE4M3, j & 3, ib[j / 4], i & 3, ia[i / 4]);
+                }
+                // the next load group goes out one load per matrix instruction, from the first
+                if constexpr (t < T::kLoadsPerStep)
+                    issue_load(std::integral_constant<int, t>{}, load_st);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
+        if constexpr (T::kLoadsPerStep > NO * NH) {
+            static_for<T::kLoadsPerStep - NO * NH>(
+                [&](auto G) { issue_load(std::integral_constant<int, NO * NH + decltype(G)::value>{}, load_st); });
+        }
+        // Every matrix instruction of the step is issued before the transition: without these
+        // (empty) uses the optimiser sinks them below its branches, into the next step.
+#pragma unroll
+        for (int i = 0; i < T::SI; ++i)
+#pragma unroll
+            for (int j = 0; j < T::SJ; ++j)
+                asm volatile("" : "+v"(acc[i][j]));
+        if constexpr (ROUTE == kRouteBS) {
+            asm volatile("" : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]));
+        }
+        transition();
+        if constexpr (ROUTE == kRouteBS) {
+            constexpr int n = T::SI * T::SJ;
+            if constexpr (n >= 2)
+                promote(std::integral_constant<int, n - 2>{});
+            promote(std::integral_constant<int, n - 1>{});
         }
     };
 
     // ---- the step stream ---------------------------------------------------------------------
-    // Before step s computes, its loads (issued STAGES-1 steps earlier) must have landed for
-    // every wave. Loads complete in order among themselves but not in order with the C stores
-    // of an epilogue, so right after an epilogue the wait is for everything.
+    // Step s reads stage s % STAGES, and while its matrix instructions run it issues the loads
+    // of step s + STAGES - 1 into stage (s - 1) % STAGES. Between the last matrix row of step s
+    // and the first of step s+1 every wave (1) has finished its reads of stage s, (2) waits for
+    // its own loads of step s+1 (vmcnt), then (3) meets the others at the barrier: after it,
+    // step s+1's operands are in LDS for everyone and stage s is free for the loads that step
+    // s+1 issues. Loads complete in order among themselves but not in order with the C stores
+    // of an epilogue, so the first wait after an epilogue is for everything.
+    int cp_tile = 0, cp_kb = 0;  // the step being computed
     int stores_pending = 0;
+    auto wait_groups = [&]() {  // all but the STAGES-2 most recent load groups have landed
+        if (stores_pending)
+            wait_vmcnt_lgkm<0>();
+        else
+            wait_vmcnt_lgkm<(STAGES - 2) * T::kLoadsPerStep>();
+        stores_pending = 0;
+    };
+    auto stage_ptr = [&](auto S) -> uint8_t* {
+        constexpr int k = decltype(S)::value;
+        return k == 0 ? st0 : k == 1 ? st1 : k == 2 ? st2 : st3;
+    };
     auto step = [&](auto S, int s) {
         constexpr int kS = decltype(S)::value;
-        constexpr int kNext = (kS + STAGES - 1) % STAGES;
-        uint8_t* cur = kS == 0 ? st0 : kS == 1 ? st1 : kS == 2 ? st2 : st3;
-        uint8_t* nxt = kNext == 0 ? st0 : kNext == 1 ? st1 : kNext == 2 ? st2 : st3;
-        const int ahead = min(STAGES - 2, total - 1 - s);  // load groups issued after step s's
-        if (stores_pending || ahead <= 0) {
-            wait_vmcnt<0>();
-        } else if (ahead == 1) {
-            wait_vmcnt<T::kLoadsPerStep>();
-        } else {
-            wait_vmcnt<(STAGES > 3 ? 2 : 1) * T::kLoadsPerStep>();
-        }
-        stores_pending = 0;
-        __builtin_amdgcn_s_barrier();
-        if (s + STAGES - 1 < total)
-            issue_loads((lds_u8*)nxt, s + STAGES - 1);
-        compute(cur);
-        const int i = s / KB;
-        if (s - i * KB == KB - 1) {
-            store_tile(i);
+        uint8_t* cur = stage_ptr(S);
+        uint8_t* nxt = stage_ptr(std::integral_constant<int, (kS + 1) % STAGES>{});
+        uint8_t* ld = stage_ptr(std::integral_constant<int, (kS + STAGES - 1) % STAGES>{});
+        plan_loads(s + STAGES - 1 < total);
+        // (unconditional: after the last step it waits for the trailing loads and reads a
+        // stage nobody uses, which keeps the control flow, and the compiler's own LDS waits,
+        // simple)
+        rows(cur, (lds_u8*)ld, [&]() {
+            wait_groups();
+            __builtin_amdgcn_s_barrier();
+            read_head(nxt);
+        });
+        if (++cp_kb == KB) {
+            store_tile(cp_tile);
             stores_pending = 1;
+            cp_kb = 0;
+            ++cp_tile;
         }
     };
-
-    if (0 < total)
-        issue_loads((lds_u8*)st0, 0);
-    if (STAGES > 2 && 1 < total)
-        issue_loads((lds_u8*)st1, 1);
-    if (STAGES > 3 && 2 < total)
-        issue_loads((lds_u8*)st2, 2);
+    if (total > 0) {
+        static_for<STAGES - 1>([&](auto S) {
+            plan_loads(decltype(S)::value < total);
+            issue_group((lds_u8*)stage_ptr(S));
+        });
+        wait_groups();
+        __builtin_amdgcn_s_barrier();
+        read_head(st0);
+    }
     for (int s = 0; s < total; s += STAGES) {
         step(std::integral_constant<int, 0>{}, s);
         if (s + 1 < total)
@@ -377,6 +488,8 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
                 step(std::integral_constant<int, 3>{}, s + 3);
         }
     }
+    // the trailing load groups write LDS: let them land before the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(0);
 }
 
 // ---- host side ---------------------------------------------------------------------------
@@ -421,17 +534,18 @@ static hipError_t launch_tile(const GemmArgs& a, const GemmConfig& c)
 }
 
 // Instantiated shapes: {BM, BN, WM, WN, STAGES}. Index = GemmConfig::variant.
-#define FP8BS_VARIANTS(X)        \
-    X(0, 128, 128, 2, 2, 3)      \
-    X(1, 256, 256, 4, 2, 2)      \
-    X(2, 256, 256, 2, 4, 2)      \
-    X(3, 128, 256, 2, 2, 3)      \
-    X(4, 256, 128, 2, 2, 3)      \
-    X(5, 128, 256, 2, 4, 3)      \
-    X(6, 256, 128, 4, 2, 3)      \
-    X(7, 128, 64, 2, 1, 3)       \
-    X(8, 256, 128, 4, 2, 2)      \
-    X(9, 128, 128, 2, 2, 4)
+#define FP8BS_VARIANTS(X)     \
+    X(0, 128, 128, 2, 2, 3)   \
+    X(1, 256, 256, 4, 2, 2)   \
+    X(2, 256, 256, 2, 4, 2)   \
+    X(3, 128, 256, 2, 2, 3)   \
+    X(4, 256, 128, 2, 2, 3)   \
+    X(5, 128, 256, 2, 4, 3)   \
+    X(6, 256, 128, 4, 2, 3)   \
+    X(7, 128, 64, 2, 1, 3)    \
+    X(8, 256, 128, 4, 2, 2)   \
+    X(9, 128, 128, 2, 2, 4)   \
+    X(10, 128, 128, 2, 2, 2)
 
 const VariantInfo* variant_info(int v)
 {

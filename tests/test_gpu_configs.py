@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 TILES = [(128, 128, 2, 2, 3), (256, 256, 4, 2, 2), (256, 256, 2, 4, 2), (128, 256, 2, 2, 3),
          (256, 128, 2, 2, 3), (128, 256, 2, 4, 3), (256, 128, 4, 2, 3), (128, 64, 2, 1, 3),
-         (256, 128, 4, 2, 2), (128, 128, 2, 2, 4)]
+         (256, 128, 4, 2, 2), (128, 128, 2, 2, 4), (128, 128, 2, 2, 2)]
 
 
 @pytest.fixture(scope="module")

@@ -103,17 +103,29 @@ __device__ __forceinline__ void static_for(F&& f)
 }
 
 // Tile u of the persistent order -> output tile (tm, tn). Workgroup ids are dispatched
-// round-robin over the 8 XCDs, so with a grid that is a multiple of 8, tile u runs on XCD u % 8.
-// With xcd_remap, XCD x owns the contiguous range [x*T/8, (x+1)*T/8) of the tile order, and the
-// workgroups of one XCD walk it together. The order visits group_m tile rows at a time, row
-// index fastest, so a window of concurrently running tiles is a compact block of the grid.
-__device__ __forceinline__ void tile_of(int u, int tiles_m, int tiles_n, int group_m, int xcd_remap,
+// round-robin over the 8 XCDs, so with a grid that is a multiple of 8, tile u runs on XCD u % 8,
+// and tiles [r*grid, (r+1)*grid) run at the same time (round r). The base order t visits
+// group_m tile rows at a time, row index fastest, so a window of consecutive t is a compact
+// block of the output. The mapping u -> t is a permutation of [0, T):
+//  * xcd_remap 0: t = u (the XCDs interleave tile by tile);
+//  * xcd_remap 1: XCD x owns the contiguous range [x*T/8, (x+1)*T/8) of t (needs T % 8 == 0);
+//  * xcd_remap 2: within each full round, XCD x owns the contiguous eighth
+//    [r*grid + x*grid/8, r*grid + (x+1)*grid/8): every XCD works on its own compact block of
+//    the same window of the output at the same time (a partial last round keeps t = u).
+__device__ __forceinline__ void tile_of(int u, int grid, int tiles_m, int tiles_n, int group_m, int xcd_remap,
                                         int& tm, int& tn)
 {
     const int T = tiles_m * tiles_n;
     int t = u;
-    if (xcd_remap && (T & 7) == 0)
+    if (xcd_remap == 1 && (T & 7) == 0) {
         t = (u & 7) * (T >> 3) + (u >> 3);
+    } else if (xcd_remap == 2 && (grid & 7) == 0) {
+        const int r0 = u - u % grid;
+        if (r0 + grid <= T) {
+            const int l = u - r0;
+            t = r0 + (l & 7) * (grid >> 3) + (l >> 3);
+        }
+    }
     const int per_group = group_m * tiles_n;
     const int g = t / per_group;
     const int first_m = g * group_m;
@@ -167,7 +179,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     int load_tile = -1;          // tile index (in this workgroup's list) the descriptors describe
     auto setup_loads = [&](int i) {
         int tm, tn;
-        tile_of((int)blockIdx.x + i * grid, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
+        tile_of((int)blockIdx.x + i * grid, grid, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
         const int m0 = tm * BM, n0 = tn * BN;
 #pragma unroll
         for (int g = 0; g < T::kLoadsA; ++g) {
@@ -283,7 +295,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     // store per lane and pair, sixteen rows x 64 contiguous bytes per store instruction.
     auto store_tile = [&](int i) {
         int tm, tn;
-        tile_of((int)blockIdx.x + i * grid, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
+        tile_of((int)blockIdx.x + i * grid, grid, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
         const int mbase = tm * BM + wm * T::TM + frow;
         const int nbase = tn * BN + wn * T::TN + 8 * (int)q;
 #pragma unroll

@@ -130,7 +130,9 @@ typedef struct {
     int waves_n;
     int stages;      /* LDS buffers in the load ring (prefetch depth stages-1 K blocks)        */
     int group_m;     /* tile rows walked together by consecutive tiles (>= 1)                  */
-    int xcd_remap;   /* 1: hand each of the 8 XCDs a contiguous range of tiles (L2 locality)   */
+    int xcd_remap;   /* tile order over the 8 XCDs (each has its own L2): 0 round-robin,       *
+                      * 1 each XCD a contiguous eighth of all tiles, 2 each XCD a contiguous   *
+                      * eighth of every set of tiles resident at the same time                 */
     int persistent;  /* 1: one workgroup per CU slot walks several tiles; 0: one per tile      */
 } fp8bs_config;
 

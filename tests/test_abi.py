@@ -91,8 +91,8 @@ def test_select_config_is_shape_driven(fb):
     assert ((4096 + nn.block_m - 1) // nn.block_m) * (2048 // nn.block_n) >= 256
     mx = fb.fp8bs_select_config(fb.ROUTE_MX, 128, 192, 256)
     assert 192 % mx.block_n == 0
-    wide = fb.fp8bs_select_config(fb.ROUTE_BS, 4096, 65536, 1536)  # 1024-tile bands: round-robin order
-    assert (wide.block_m, wide.block_n) == (256, 256) and wide.xcd_remap == 0
+    wide = fb.fp8bs_select_config(fb.ROUTE_BS, 4096, 65536, 1536)  # 1024-tile bands: round-local order
+    assert (wide.block_m, wide.block_n) == (256, 256) and wide.xcd_remap == 2
     for route, shape in ((fb.ROUTE_BS, (4096, 65536, 1536)), (fb.ROUTE_MX, (16384, 8192, 1280)),
                          (fb.ROUTE_BS, (128, 256, 512)), (fb.ROUTE_BS, (1, 128, 128))):
         c = fb.fp8bs_select_config(route, *shape)

@@ -55,7 +55,8 @@ ROUTE_BS, ROUTE_MX = 0, 1
 class Config(ctypes.Structure):
     """fp8bs_config of include/fp8bs.h."""
     _fields_ = [(n, ctypes.c_int) for n in
-                ("block_m", "block_n", "waves_m", "waves_n", "stages", "group_m", "xcd_remap", "persistent")]
+                ("block_m", "block_n", "waves_m", "waves_n", "stages", "group_m", "xcd_remap", "persistent",
+                 "pingpong")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -44,7 +44,7 @@ int find_variant(const fp8bs_config& c)
         if (!vi)
             return -1;
         if (vi->block_m == c.block_m && vi->block_n == c.block_n && vi->waves_m == c.waves_m &&
-            vi->waves_n == c.waves_n && vi->stages == c.stages)
+            vi->waves_n == c.waves_n && vi->stages == c.stages && vi->pingpong == c.pingpong)
             return v;
     }
 }
@@ -58,6 +58,7 @@ fp8bs_config make_config(int variant, int group_m, int xcd_remap, int persistent
     c.waves_m = vi->waves_m;
     c.waves_n = vi->waves_n;
     c.stages = vi->stages;
+    c.pingpong = vi->pingpong;
     c.group_m = group_m;
     c.xcd_remap = xcd_remap;
     c.persistent = persistent;

@@ -52,7 +52,7 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int kLdsCapacity = 160 * 1024;
 
-template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES>
+template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES, int PP>
 struct Tile {
     static constexpr int kWaves = WM * WN;
     static constexpr int kThreads = kWaves * 64;
@@ -80,6 +80,7 @@ struct Tile {
     static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
     static_assert(STAGES * kStageBytes <= kLdsCapacity, "LDS capacity");
     static_assert(kLoadsPerStep * (STAGES - 1) <= 63, "vmcnt range");
+    static_assert(PP == 0 || (STAGES == 2 && kWaves == 8), "ping-pong: two stages, two groups of four waves");
 };
 
 // s_waitcnt for vmcnt <= N and lgkmcnt == 0 (expcnt left unconstrained).
@@ -88,6 +89,39 @@ __device__ __forceinline__ void wait_vmcnt_lgkm()
 {
     static_assert(N >= 0 && N <= 63, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// s_waitcnt for lgkmcnt == 0 only.
+__device__ __forceinline__ void wait_lgkm0()
+{
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
+}
+
+// Buffer resource for a byte buffer starting at `base` (range check at 2^31 - 1 bytes).
+__device__ __forceinline__ v4i buffer_desc(const void* base)
+{
+    const uint64_t a = (uint64_t)base;
+    return v4i{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), 0x7FFFFFFF, 0x00020000};
+}
+
+// Global -> LDS copy of BYTES (16 or 4) per lane: lane l reads rs[voff + soff] and writes LDS
+// byte address dst + BYTES * l. Issued through inline assembly, so the compiler tracks neither
+// the LDS write nor the vmcnt it adds: every read of the stage it fills waits for it with an
+// explicit vmcnt wait and barrier (the compiler's own tracking loses the stage at loop
+// back-edges and would wait for loads that were just issued). dst and soff are uniform.
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const v4i& rs, uint32_t dst, int voff, int soff)
+{
+    if constexpr (BYTES == 16)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :
+                     : "s"(dst), "v"(voff), "s"(rs), "s"(soff)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                     :
+                     : "s"(dst), "v"(voff), "s"(rs), "s"(soff)
+                     : "memory", "m0");
 }
 
 // Calls f(std::integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
@@ -135,14 +169,14 @@ __device__ __forceinline__ void tile_of(int u, int grid, int tiles_m, int tiles_
     tn = r / gm;
 }
 
-template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES>
+template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES, int PP>
 __global__ void __launch_bounds__(WM * WN * 64)
 gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
             const uint8_t* __restrict__ B, const void* __restrict__ b_scale,
             uint16_t* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
             int group_m, int xcd_remap)
 {
-    using T = Tile<ROUTE, BM, BN, WM, WN, STAGES>;
+    using T = Tile<ROUTE, BM, BN, WM, WN, STAGES, PP>;
     // One LDS array per stage: the stage of every read is known at compile time, so the
     // compiler can tell LDS-DMA writes to one stage from reads of another and adds no waits.
     __shared__ __attribute__((aligned(1024))) uint8_t st0[T::kStageBytes];
@@ -162,12 +196,10 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     const int my_tiles = (int)blockIdx.x < T_total ? (T_total - 1 - (int)blockIdx.x) / grid + 1 : 0;
     const int total = my_tiles * KB;
 
-    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, 0x7FFFFFFF, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc((void*)B, (short)0, 0x7FFFFFFF, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsSA =
-        __builtin_amdgcn_make_buffer_rsrc((void*)a_scale, (short)0, 0x7FFFFFFF, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rsSB =
-        __builtin_amdgcn_make_buffer_rsrc((void*)b_scale, (short)0, 0x7FFFFFFF, 0x00020000);
+    const v4i rsA = buffer_desc(A);
+    const v4i rsB = buffer_desc(B);
+    const v4i rsSA = buffer_desc(a_scale);
+    const v4i rsSB = buffer_desc(b_scale);
 
     // ---- per-tile load descriptors (recomputed when the stream enters a new tile) ---------
     // A wave's load g covers 8 rows (1 KB): lane l writes physical chunk l&7 of row l>>3, which
@@ -235,26 +267,24 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
         ld_kbv = kb;
     };
     // Load g of the planned group into stage st: A rows, then B rows, then block scales.
+    auto lds_addr = [&](lds_u8* p) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)p); };
     auto issue_load = [&](auto G, lds_u8* st) {
         constexpr int g = decltype(G)::value;
-        const int koff = ld_kbv * 128;
+        const int koff = __builtin_amdgcn_readfirstlane(ld_kbv * 128);
         if constexpr (g < T::kLoadsA) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void*)(st + (wave * T::kLoadsA + g) * 1024), 16,
-                                                     (int)voffA[g], koff, 0, 0);
+            lds_dma<16>(rsA, lds_addr(st + (wave * T::kLoadsA + g) * 1024), (int)voffA[g], koff);
         } else if constexpr (g < T::kLoadsA + T::kLoadsB) {
             constexpr int gb = g - T::kLoadsA;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, (lds_void*)(st + T::kABytes + (wave * T::kLoadsB + gb) * 1024),
-                                                     16, (int)voffB[gb], koff, 0, 0);
+            lds_dma<16>(rsB, lds_addr(st + T::kABytes + (wave * T::kLoadsB + gb) * 1024), (int)voffB[gb], koff);
         } else {
             constexpr int gs = g - T::kLoadsA - T::kLoadsB;
             lds_u8* sS = st + T::kABytes + T::kBBytes;
             const int u = min(wave * T::kLoadsS + gs, T::kScaleLoads - 1);  // uniform
-            const int soff = __builtin_amdgcn_readfirstlane(ld_kbv * (int)kstrS[gs]);  // uniform
-            if (u < T::kScaleLoadsA)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsSA, (lds_void*)(sS + u * 256), 4, (int)voffS[gs], soff, 0, 0);
-            else
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rsSB, (lds_void*)(sS + T::kSABytes + (u - T::kScaleLoadsA) * 256),
-                                                         4, (int)voffS[gs], soff, 0, 0);
+            const int soff = __builtin_amdgcn_readfirstlane(ld_kbv * (int)kstrS[gs]);
+            const bool is_a = u < T::kScaleLoadsA;
+            const v4i rs = is_a ? rsSA : rsSB;
+            lds_u8* dst = is_a ? sS + u * 256 : sS + T::kSABytes + (u - T::kScaleLoadsA) * 256;
+            lds_dma<4>(rs, lds_addr(dst), (int)voffS[gs], soff);
         }
     };
     auto issue_group = [&](lds_u8* st) {
@@ -321,6 +351,176 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
         }
     };
 
+    if constexpr (PP) {
+    // ---- ping-pong schedule ------------------------------------------------------------------
+    // Waves w and w+4 share a SIMD, so the two groups (waves 0-3 and 4-7) each hold one wave of
+    // every SIMD. Each group alternates a memory phase (read all of the step's fragments and
+    // scales from LDS into registers) with a matrix phase (the step's matrix instructions on
+    // those registers), with a barrier after each phase; group 1 starts one barrier late, so on
+    // every SIMD one wave runs matrix instructions while the other reads its next operands.
+    // With phase 2t = group 0 reading step t and phase 2t+1 = group 0 computing step t while
+    // group 1 reads it, stage t % 2 is read in phases 2t and 2t+1 and is free from phase 2t+2.
+    // The loads of step t+1 go out from phase 2t: group 0's share at the start of its memory
+    // phase for step t, group 1's share during its matrix phase for step t-1 (one load per
+    // matrix instruction). Each wave waits for its own share before the barrier that opens
+    // phase 2t+2, so every load of step t+1 has landed when group 0 starts reading it.
+    constexpr int GA = (T::SI + 3) / 4;  // MX: packed scale dwords per wave (one per 64 rows)
+    constexpr int GB = (T::SJ + 3) / 4;
+    struct Frags {
+        v8i a[T::SI];
+        v8i b[T::SJ];
+        float sa[ROUTE == kRouteBS ? T::SI : 1];  // BS: a_s of this lane's row in sub-tile row i
+        float sb;                                  // BS: b_s of the wave's weight block
+        int ia[GA];                                // MX: packed activation scale dwords
+        int ib[GB];                                // MX: packed weight scale dwords
+    };
+    auto read_all = [&](const uint8_t* st, Frags& F) {
+        const uint8_t* sA = st + (wm * T::TM) * 128;
+        const uint8_t* sB = st + T::kABytes + (wn * T::TN) * 128;
+        const uint8_t* sS = st + T::kABytes + T::kBBytes;
+#pragma unroll
+        for (int i = 0; i < T::SI; ++i)
+            F.a[i] = frag(sA + i * 16 * 128);
+#pragma unroll
+        for (int j = 0; j < T::SJ; ++j)
+            F.b[j] = frag(sB + j * 16 * 128);
+        if constexpr (ROUTE == kRouteBS) {
+            const float* sa = (const float*)sS + wm * T::TM + frow;
+#pragma unroll
+            for (int i = 0; i < T::SI; ++i)
+                F.sa[i] = sa[16 * i];
+            F.sb = ((const float*)(sS + T::kSABytes))[(wn * T::TN) >> 7];
+        } else {
+#pragma unroll
+            for (int g = 0; g < GA; ++g)
+                F.ia[g] = ((const int*)sS)[(wm * T::TM / 64 + g) * 64 + lane];
+#pragma unroll
+            for (int g = 0; g < GB; ++g)
+                F.ib[g] = ((const int*)(sS + T::kSABytes))[(wn * T::TN / 64 + g) * 64 + lane];
+        }
+    };
+    // The step's matrix instructions, sub-tile row by row (route BS: each promote two
+    // instructions behind its instruction); hook(t) runs after instruction t.
+    v4f p[3];
+    auto mma = [&](const Frags& F, auto&& hook) {
+        float srow[T::SI];
+        if constexpr (ROUTE == kRouteBS) {
+#pragma unroll
+            for (int i = 0; i < T::SI; ++i)
+                srow[i] = F.sa[i] * F.sb;
+        }
+        auto promote = [&](auto Tc) {
+            constexpr int t = decltype(Tc)::value;
+            acc[t / T::SJ][t % T::SJ] += p[t % 3] * srow[t / T::SJ];
+        };
+        static_for<T::SI>([&](auto I) {
+            constexpr int i = decltype(I)::value;
+            static_for<T::SJ>([&](auto J) {
+                constexpr int j = decltype(J)::value;
+                constexpr int t = i * T::SJ + j;
+                if constexpr (ROUTE == kRouteBS) {
+                    p[t % 3] = mfma_f8(F.b[j], F.a[i], v4f{0.f, 0.f, 0.f, 0.f});
+                    if constexpr (t >= 2)
+                        promote(std::integral_constant<int, t - 2>{});
+                } else {
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        F.b[j], F.a[i], acc[i][j], kFmtE4M3, kFmtE4M3, j & 3, F.ib[j / 4], i & 3, F.ia[i / 4]);
+                }
+                hook(std::integral_constant<int, t>{});
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        });
+        if constexpr (ROUTE == kRouteBS) {
+            constexpr int n = T::SI * T::SJ;
+            promote(std::integral_constant<int, n - 2>{});
+            promote(std::integral_constant<int, n - 1>{});
+        }
+        // keep every instruction of the phase inside the phase (the optimiser would otherwise
+        // sink them below the following branches)
+#pragma unroll
+        for (int i = 0; i < T::SI; ++i)
+#pragma unroll
+            for (int j = 0; j < T::SJ; ++j)
+                asm volatile("" : "+v"(acc[i][j]));
+    };
+    int cp_tile = 0, cp_kb = 0;  // the step being computed
+    auto finish_step = [&]() {
+        if (++cp_kb == KB) {
+            store_tile(cp_tile);
+            cp_kb = 0;
+            ++cp_tile;
+        }
+    };
+    const int grp = wave >> 2;
+    if (total > 0) {
+        plan_loads(true);
+        issue_group((lds_u8*)st0);  // step 0, every wave
+        if (grp == 1) {
+            plan_loads(1 < total);
+            issue_group((lds_u8*)st1);  // group 1's share of step 1
+        }
+        // (group 1 waits for its share of step 1 too: with nothing in flight at the top of the
+        // step loop, the compiler's own LDS waits there stay exact)
+        wait_vmcnt_lgkm<0>();
+        __builtin_amdgcn_s_barrier();
+        Frags F;
+        if (grp == 0) {
+            auto step0 = [&](auto S, int t) {
+                constexpr int k = decltype(S)::value;
+                uint8_t* cur = k == 0 ? st0 : st1;
+                uint8_t* oth = k == 0 ? st1 : st0;
+                // memory phase: this group's share of step t+1's loads, then step t's operands
+                plan_loads(t + 1 < total);
+                issue_group((lds_u8*)oth);
+                read_all(cur, F);
+                wait_lgkm0();
+                __builtin_amdgcn_s_barrier();
+                // matrix phase
+                mma(F, [&](auto) {});
+                finish_step();
+                wait_vmcnt_lgkm<0>();  // own loads of step t+1
+                __builtin_amdgcn_s_barrier();
+            };
+            for (int t = 0; t < total; t += 2) {
+                step0(std::integral_constant<int, 0>{}, t);
+                if (t + 1 < total)
+                    step0(std::integral_constant<int, 1>{}, t + 1);
+            }
+            __builtin_amdgcn_s_barrier();  // matches group 1's extra first barrier
+        } else {
+            __builtin_amdgcn_s_barrier();  // one phase behind group 0
+            auto step1 = [&](auto S, int t) {
+                constexpr int k = decltype(S)::value;
+                uint8_t* cur = k == 0 ? st0 : st1;
+                // memory phase: step t's operands; own loads of step t+1 must have landed
+                read_all(cur, F);
+                wait_vmcnt_lgkm<0>();
+                __builtin_amdgcn_s_barrier();
+                // matrix phase, issuing this group's share of step t+2 into the stage just read
+                plan_loads(t + 2 < total);
+                mma(F, [&](auto Tc) {
+                    constexpr int tt = decltype(Tc)::value;
+                    if constexpr (tt < T::kLoadsPerStep)
+                        issue_load(std::integral_constant<int, tt>{}, (lds_u8*)cur);
+                });
+                if constexpr (T::kLoadsPerStep > T::SI * T::SJ) {
+                    static_for<T::kLoadsPerStep - T::SI * T::SJ>([&](auto G) {
+                        issue_load(std::integral_constant<int, T::SI * T::SJ + decltype(G)::value>{}, (lds_u8*)cur);
+                    });
+                }
+                finish_step();
+                __builtin_amdgcn_s_barrier();
+            };
+            for (int t = 0; t < total; t += 2) {
+                step1(std::integral_constant<int, 0>{}, t);
+                if (t + 1 < total)
+                    step1(std::integral_constant<int, 1>{}, t + 1);
+            }
+        }
+    }
+    // the trailing load groups write LDS: let them land before the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(0);
+    } else {
     // ---- registers of the step being computed ----------------------------------------------
     // The operand with fewer fragments per wave is held whole; the other is streamed through a
     // two-deep ring (fragment o+1 is read while the instructions of fragment o run).
@@ -371,6 +571,11 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     // (acc += partial * a_s*b_s) is issued two instructions later, once the result is ready, so
     // the matrix core never waits on the vector ALU. Scheduling barriers keep that order.
     // `transition` runs after the last instruction is issued and before the last two promotes.
+    // With three or more stages the loads of a step have a whole extra step to land, so they
+    // are spread evenly over the step; with two they must land by the end of the step that
+    // issues them, so they go out from its first instruction on.
+    constexpr int kLoadSpacing =
+        STAGES >= 3 && NO * NH >= 2 * T::kLoadsPerStep ? (NO * NH) / T::kLoadsPerStep : 1;
     v4f p[3];
     auto rows = [&](const uint8_t* st, lds_u8* load_st, auto&& transition) {
         const uint8_t* sO = streamed(st);
@@ -407,9 +612,11 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                         b, a, acc[i][j], kFmtE4M3, kFmtE4M3, j & 3, ib[j / 4], i & 3, ia[i / 4]);
                 }
-                // the next load group goes out one load per matrix instruction, from the first
-                if constexpr (t < T::kLoadsPerStep)
-                    issue_load(std::integral_constant<int, t>{}, load_st);
+                // the next load group goes out spread over the step (kLoadSpacing instructions
+                // apart): a burst of loads fills the memory path's in-flight capacity and
+                // stalls the issuing wave, matrix instructions and all
+                if constexpr (t % kLoadSpacing == 0 && t / kLoadSpacing < T::kLoadsPerStep)
+                    issue_load(std::integral_constant<int, t / kLoadSpacing>{}, load_st);
                 __builtin_amdgcn_sched_barrier(0);
             });
         });
@@ -502,6 +709,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     }
     // the trailing load groups write LDS: let them land before the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt(0);
+    }
 }
 
 // ---- host side ---------------------------------------------------------------------------
@@ -521,14 +729,14 @@ int device_cus()
     return cus[dev];
 }
 
-template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES>
+template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES, int PP>
 static hipError_t launch_tile(const GemmArgs& a, const GemmConfig& c)
 {
-    using T = Tile<ROUTE, BM, BN, WM, WN, STAGES>;
+    using T = Tile<ROUTE, BM, BN, WM, WN, STAGES, PP>;
     // workgroups that fit on one CU at once (LDS and registers), once per instantiation
     static const int per_cu = [] {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_kernel<ROUTE, BM, BN, WM, WN, STAGES>,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_kernel<ROUTE, BM, BN, WM, WN, STAGES, PP>,
                                                          T::kThreads, 0) != hipSuccess || n < 1)
             n = 1;
         return n;
@@ -539,30 +747,32 @@ static hipError_t launch_tile(const GemmArgs& a, const GemmConfig& c)
     int grid = device_cus() * per_cu;
     if (c.persistent == 0 || grid > T_total)
         grid = T_total;
-    hipLaunchKernelGGL((gemm_kernel<ROUTE, BM, BN, WM, WN, STAGES>), dim3(grid), dim3(T::kThreads), 0, a.stream,
+    hipLaunchKernelGGL((gemm_kernel<ROUTE, BM, BN, WM, WN, STAGES, PP>), dim3(grid), dim3(T::kThreads), 0, a.stream,
                        (const uint8_t*)a.A, a.a_scale, (const uint8_t*)a.B, a.b_scale, (uint16_t*)a.C, a.M, a.N,
                        a.K, tiles_m, tiles_n, c.group_m > 0 ? c.group_m : 1, c.xcd_remap);
     return hipGetLastError();
 }
 
-// Instantiated shapes: {BM, BN, WM, WN, STAGES}. Index = GemmConfig::variant.
-#define FP8BS_VARIANTS(X)     \
-    X(0, 128, 128, 2, 2, 3)   \
-    X(1, 256, 256, 4, 2, 2)   \
-    X(2, 256, 256, 2, 4, 2)   \
-    X(3, 128, 256, 2, 2, 3)   \
-    X(4, 256, 128, 2, 2, 3)   \
-    X(5, 128, 256, 2, 4, 3)   \
-    X(6, 256, 128, 4, 2, 3)   \
-    X(7, 128, 64, 2, 1, 3)    \
-    X(8, 256, 128, 4, 2, 2)   \
-    X(9, 128, 128, 2, 2, 4)   \
-    X(10, 128, 128, 2, 2, 2)
+// Instantiated shapes: {BM, BN, WM, WN, STAGES, ping-pong}. Index = GemmConfig::variant.
+#define FP8BS_VARIANTS(X)        \
+    X(0, 128, 128, 2, 2, 3, 0)   \
+    X(1, 256, 256, 4, 2, 2, 0)   \
+    X(2, 256, 256, 2, 4, 2, 0)   \
+    X(3, 128, 256, 2, 2, 3, 0)   \
+    X(4, 256, 128, 2, 2, 3, 0)   \
+    X(5, 128, 256, 2, 4, 3, 0)   \
+    X(6, 256, 128, 4, 2, 3, 0)   \
+    X(7, 128, 64, 2, 1, 3, 0)    \
+    X(8, 256, 128, 4, 2, 2, 0)   \
+    X(9, 128, 128, 2, 2, 4, 0)   \
+    X(10, 128, 128, 2, 2, 2, 0)  \
+    X(11, 256, 128, 4, 2, 2, 1)  \
+    X(12, 128, 256, 2, 4, 2, 1)
 
 const VariantInfo* variant_info(int v)
 {
     static const VariantInfo table[] = {
-#define X(id, bm, bn, wm, wn, st) {bm, bn, wm, wn, st},
+#define X(id, bm, bn, wm, wn, st, pp) {bm, bn, wm, wn, st, pp},
         FP8BS_VARIANTS(X)
 #undef X
     };
@@ -577,18 +787,18 @@ static constexpr bool mx_fits()
     return (BM / WM) % 64 == 0 && (BN / WN) % 64 == 0 && ST * (BM * 132 + BN * 132) <= kLdsCapacity;
 }
 
-template <int BM, int BN, int WM, int WN, int ST>
+template <int BM, int BN, int WM, int WN, int ST, int PP>
 static hipError_t launch_variant(int route, const GemmArgs& a, const GemmConfig& c)
 {
     constexpr int TN = BN / WN;
     if (route == kRouteBS) {
         if constexpr (TN <= 128 && 128 % TN == 0)
-            return launch_tile<kRouteBS, BM, BN, WM, WN, ST>(a, c);
+            return launch_tile<kRouteBS, BM, BN, WM, WN, ST, PP>(a, c);
         else
             return hipErrorInvalidValue;
     }
     if constexpr (mx_fits<BM, BN, WM, WN, ST>())
-        return launch_tile<kRouteMX, BM, BN, WM, WN, ST>(a, c);
+        return launch_tile<kRouteMX, BM, BN, WM, WN, ST, PP>(a, c);
     else
         return hipErrorInvalidValue;
 }
@@ -607,9 +817,9 @@ bool variant_supports(int route, int v)
 hipError_t launch_gemm(int route, const GemmArgs& a, const GemmConfig& c)
 {
     switch (c.variant) {
-#define X(id, bm, bn, wm, wn, st) \
-    case id:                      \
-        return launch_variant<bm, bn, wm, wn, st>(route, a, c);
+#define X(id, bm, bn, wm, wn, st, pp) \
+    case id:                          \
+        return launch_variant<bm, bn, wm, wn, st, pp>(route, a, c);
         FP8BS_VARIANTS(X)
 #undef X
     default:

@@ -20,7 +20,7 @@ struct GemmArgs {
 
 // One instantiated kernel shape: BM x BN output tile, WM x WN waves, STAGES LDS buffers.
 struct VariantInfo {
-    int block_m, block_n, waves_m, waves_n, stages;
+    int block_m, block_n, waves_m, waves_n, stages, pingpong;
 };
 
 struct GemmConfig {

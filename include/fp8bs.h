@@ -134,6 +134,8 @@ typedef struct {
                       * 1 each XCD a contiguous eighth of all tiles, 2 each XCD a contiguous   *
                       * eighth of every set of tiles resident at the same time                 */
     int persistent;  /* 1: one workgroup per CU slot walks several tiles; 0: one per tile      */
+    int pingpong;    /* 1: the two halves of an 8-wave workgroup alternate, one running its    *
+                      * matrix instructions while the other reads its next operands (2 stages) */
 } fp8bs_config;
 
 /* The configuration fp8bs_gemm (route FP8BS_ROUTE_BS) or fp8mx_gemm (FP8BS_ROUTE_MX) uses for
@@ -141,7 +143,7 @@ typedef struct {
 int fp8bs_select_config(int route, int M, int N, int K, fp8bs_config *out);
 
 /* fp8bs_gemm / fp8mx_gemm with an explicit configuration. The (block_m, block_n, waves_m,
- * waves_n, stages) tuple must be one the library instantiates and valid for the route, and N
+ * waves_n, stages, pingpong) tuple must be one the library instantiates and valid for the route, and N
  * must be a multiple of block_n; otherwise FP8BS_E_CONFIG and nothing is launched. Every
  * configuration performs the same per-element arithmetic in the same order, so results are
  * bitwise identical to the plain entry point's. */

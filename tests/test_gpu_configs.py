@@ -13,9 +13,11 @@ from gpu_util import bits, dev, parity, to_dev
 pytestmark = pytest.mark.gpu
 
 
-TILES = [(128, 128, 2, 2, 3), (256, 256, 4, 2, 2), (256, 256, 2, 4, 2), (128, 256, 2, 2, 3),
-         (256, 128, 2, 2, 3), (128, 256, 2, 4, 3), (256, 128, 4, 2, 3), (128, 64, 2, 1, 3),
-         (256, 128, 4, 2, 2), (128, 128, 2, 2, 4), (128, 128, 2, 2, 2)]
+# (block_m, block_n, waves_m, waves_n, stages, pingpong)
+TILES = [(128, 128, 2, 2, 3, 0), (256, 256, 4, 2, 2, 0), (256, 256, 2, 4, 2, 0), (128, 256, 2, 2, 3, 0),
+         (256, 128, 2, 2, 3, 0), (128, 256, 2, 4, 3, 0), (256, 128, 4, 2, 3, 0), (128, 64, 2, 1, 3, 0),
+         (256, 128, 4, 2, 2, 0), (128, 128, 2, 2, 4, 0), (128, 128, 2, 2, 2, 0), (256, 128, 4, 2, 2, 1),
+         (128, 256, 2, 4, 2, 1)]
 
 
 @pytest.fixture(scope="module")
@@ -26,12 +28,13 @@ def fb():
 
 def _configs(fb, route, N):
     out = []
-    for (bm, bn, wm, wn, st), (gm, xcd, pers) in itertools.product(TILES, ((1, 0, 0), (3, 1, 1), (2, 0, 1), (2, 2, 1), (1, 2, 0))):
+    for (bm, bn, wm, wn, st, pp), (gm, xcd, pers) in itertools.product(
+            TILES, ((1, 0, 0), (3, 1, 1), (2, 0, 1), (2, 2, 1), (1, 2, 0))):
         tm, tn = bm // wm, bn // wn
         ok = (tn <= 128 and 128 % tn == 0) if route == fb.ROUTE_BS else \
             (tm % 64 == 0 and tn % 64 == 0 and st * (bm + bn) * 132 <= 160 * 1024)
         if ok and N % bn == 0:
-            out.append(fb.Config(bm, bn, wm, wn, st, gm, xcd, pers))
+            out.append(fb.Config(bm, bn, wm, wn, st, gm, xcd, pers, pp))
     return out
 
 
@@ -82,7 +85,9 @@ def test_invalid_configs_rejected(fb):
     for cfg in (fb.Config(64, 64, 1, 1, 2, 1, 1, 1), fb.Config(256, 256, 2, 2, 2, 1, 1, 1),  # not instantiated
                 fb.Config(256, 256, 4, 2, 3, 1, 1, 1),  # stages not instantiated for this tile
                 fb.Config(128, 256, 1, 2, 3, 1, 1, 1), fb.Config(256, 256, 4, 2, 2, 0, 1, 1),  # group_m < 1
-                fb.Config(128, 128, 2, 2, 3, 1, 3, 1), fb.Config(128, 128, 2, 2, 3, 1, 1, 5)):
+                fb.Config(128, 128, 2, 2, 3, 1, 3, 1), fb.Config(128, 128, 2, 2, 3, 1, 1, 5),
+                fb.Config(256, 128, 4, 2, 3, 1, 1, 1, 1),  # ping-pong needs two stages
+                fb.Config(256, 128, 4, 2, 2, 1, 1, 1, 2)):  # no such schedule
         with pytest.raises(fb.Fp8bsError) as e:
             fb.fp8bs_gemm_with_config(A, sa, Bp, sb, C, cfg)
         assert e.value.status == 4

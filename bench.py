@@ -11,8 +11,10 @@ every input already resident in HBM. Prints ONE JSON line on stdout:
   mfma_ceiling -- the matrix core's sustained rate on this workload's own operand bytes with
                   no memory traffic (the gfx950 matrix core slows down when operand bits
                   change between instructions; this is the reachable ceiling for this data)
-  per_shape    -- steady-state time of all five workloads (tiny, narrow-N, K-light, wide-N,
-                  mxfp8), TFLOP/s, % of peak, algorithmic HBM GB/s
+  per_shape    -- steady-state ("hot", back-to-back launches) time of all five workloads
+                  (tiny, narrow-N, K-light, wide-N, mxfp8), TFLOP/s, % of peak, algorithmic
+                  HBM GB/s, and the "cold" time of single launches that each follow a 1 GiB
+                  write evicting L2 and the MALL
   cpu_baseline -- the CPU oracle (fp64, OpenMP) on a bounded sample of output rows
   parity       -- sampled rows/columns of the timed output against the oracle
 
@@ -45,6 +47,7 @@ METRIC = "fp8 blockscale GEMM TFLOP/s and % of MI355X dense fp8 MFMA peak, per s
 MAIN = "narrow_n"
 KERNEL_SOURCES = ["gemm.hip", "device.hpp", "prep.hip"]
 COPY_BYTES = 256 << 20      # calibration copy for the byte counters
+COLD_SCRATCH_BYTES = 1 << 30  # written before each cold launch: more than L2 (8 x 4 MB) + MALL (256 MB)
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -142,6 +145,21 @@ class Case:
         per = max((time.perf_counter() - t0) / n, 1e-6)
         steps = int(min(2000, max(50, time_s / per)))
         return self.time_launches(steps, 0, stream) + (steps,)
+
+    def cold(self, stream, scratch, reps: int = 15):
+        """Median and min seconds of single launches, each preceded (outside the timed pair of
+        events) by a write of `scratch` large enough to evict L2 and the MALL."""
+        import torch
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        for i in range(reps):
+            scratch.fill_(i & 0xFF)
+            starts[i].record(stream)
+            self.launch()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) / 1e3 for a, b in zip(starts, ends))
+        return t[len(t) // 2], t[0]
 
     def free(self):
         for k in ("A", "sa", "B", "sb", "C"):
@@ -339,6 +357,7 @@ def main() -> int:
         names = [MAIN] + ([args.only] if args.only != MAIN else [])
     main_row = None
     with torch.cuda.stream(stream):
+        scratch = torch.empty(COLD_SCRATCH_BYTES, dtype=torch.uint8, device="cuda:0")
         for name in names:
             case = Case(name, 0, stream)
             if name == MAIN:
@@ -352,6 +371,9 @@ def main() -> int:
                        tflops=round(tflops, 1), pct_peak=round(100 * tflops / PEAK_FP8_TFLOPS, 2),
                        hbm_gbs_algorithmic=round(nbytes / ev / 1e9, 1), timed_launches=steps,
                        config=case.config)
+            cold_med, cold_min = case.cold(stream, scratch)
+            row.update(cold_us=round(cold_med * 1e6, 2), cold_min_us=round(cold_min * 1e6, 2),
+                       cold_tflops=round(case.flops / cold_med / 1e12, 1))
             log(f"[bench] {name}: {row}")
             if name == MAIN:
                 row["parity"] = sampled_parity(case)

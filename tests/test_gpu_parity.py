@@ -1,8 +1,9 @@
 """Parity of the HIP path (through the C ABI) with the oracle, on the GPU.
 
 Small shapes are compared in full, including ragged M tails and several tiles in each
-direction; the five bench workloads are compared on seeded samples of whole rows and whole
-columns (the oracle computes each element independently, so a sample is exact)."""
+direction. The four large benchmark workloads are compared in full for seed 0 and on seeded
+samples of 512 whole rows and 512 whole columns for seeds 1-3 (the oracle computes each
+element independently, so a sample is exact)."""
 import numpy as np
 import pytest
 
@@ -43,30 +44,45 @@ def test_mx_small_full(fb, oracle, M, N, K, seed):
     parity(got, ref, f"mx {M}x{N}x{K} seed {seed}")
 
 
-def _sampled(M, N, seed, n=48):
+def _sampled(M, N, seed, n=512):
     return workload.sample_indices(M, n, seed), workload.sample_indices(N, n, seed + 1)
 
 
-@pytest.mark.parametrize("name", ["narrow_n", "k_light", "wide_n"])
-def test_bs_workload_sampled(fb, oracle, name):
+def _inputs(name, seed):
     cfg = workload.CONFIGS[name]
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
-    x = workload.bs_inputs(M, N, K, 0)
-    got = run_bs(fb, x)
-    rows, cols = _sampled(M, N, 0)
-    _, ref_rows = oracle.bs_gemm(x.A, x.a_scale, x.B, x.b_scale, rows=rows)
-    parity(got[rows], ref_rows, f"{name} rows")
-    _, ref_cols = oracle.bs_gemm(x.A, x.a_scale, x.B, x.b_scale, cols=cols)
-    parity(got[:, cols], ref_cols, f"{name} cols")
+    if cfg["route"] == "bs":
+        return cfg, workload.bs_inputs(M, N, K, seed)
+    return cfg, workload.mx_inputs(M, N, K, seed)
 
 
-def test_mx_workload_sampled(fb, oracle):
-    cfg = workload.CONFIGS["mxfp8"]
-    M, N, K = cfg["M"], cfg["N"], cfg["K"]
-    y = workload.mx_inputs(M, N, K, 0)
-    got = run_mx(fb, y)
-    rows, cols = _sampled(M, N, 0)
-    _, ref_rows = oracle.mx_gemm(y.A, y.a_e8m0, y.B, y.b_e8m0, rows=rows)
-    parity(got[rows], ref_rows, "mxfp8 rows")
-    _, ref_cols = oracle.mx_gemm(y.A, y.a_e8m0, y.B, y.b_e8m0, cols=cols)
-    parity(got[:, cols], ref_cols, "mxfp8 cols")
+def _run(fb, cfg, x):
+    return run_bs(fb, x) if cfg["route"] == "bs" else run_mx(fb, x)
+
+
+def _ref(oracle, cfg, x, rows=None, cols=None):
+    if cfg["route"] == "bs":
+        return oracle.bs_gemm(x.A, x.a_scale, x.B, x.b_scale, rows=rows, cols=cols)[1]
+    return oracle.mx_gemm(x.A, x.a_e8m0, x.B, x.b_e8m0, rows=rows, cols=cols)[1]
+
+
+@pytest.mark.parametrize("name", ["narrow_n", "k_light", "wide_n", "mxfp8"])
+def test_workload_full_seed0(fb, oracle, name):
+    """Every element of C at the benchmark size, in the launch configuration the benchmark
+    times (the library's own choice for the shape), seed 0."""
+    cfg, x = _inputs(name, 0)
+    got = _run(fb, cfg, x)
+    ref = _ref(oracle, cfg, x)
+    parity(got, ref, f"{name} full C seed 0")
+
+
+@pytest.mark.parametrize("name", ["narrow_n", "k_light", "wide_n", "mxfp8"])
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_workload_sampled(fb, oracle, name, seed):
+    """512 whole rows and 512 whole columns of C at the benchmark size for seeds 1-3 (the
+    oracle computes each element on its own, so a sample is exact)."""
+    cfg, x = _inputs(name, seed)
+    got = _run(fb, cfg, x)
+    rows, cols = _sampled(cfg["M"], cfg["N"], seed)
+    parity(got[rows], _ref(oracle, cfg, x, rows=rows), f"{name} seed {seed} rows")
+    parity(got[:, cols], _ref(oracle, cfg, x, cols=cols), f"{name} seed {seed} cols")

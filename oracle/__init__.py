@@ -11,6 +11,8 @@ Gemm", Procedure step 1: fp32 dequantise, matmul, round to bf16; page "aiter PR 
 
     BS:  C[m,n] = bf16( sum_kb a_s[m,kb] * b_s[n//128,kb] * sum_{k in kb} A[m,k] B[n,k] )
     MX:  C[m,n] = bf16( sum_g 2^(ea[m,g]-127) 2^(eb[n,g]-127) sum_{k in g} A[m,k] B[n,k] )
+    PT:  C[m,n] = bf16( a_s[m] * b_s[n] * sum_k A[m,k] B[n,k] )   (the promote-free twin,
+         page "Flydsl Fp8 Blockscale Gemm", Bottleneck diagnosis item 2)
 
 with block sums exact in fp64 and one round-to-nearest-even from fp64 to bf16.
 
@@ -54,7 +56,7 @@ class Oracle:
             raise FileNotFoundError(f"oracle library not built: {path}")
         self.path = path
         lib = ctypes.CDLL(path)
-        for name in ("oracle_bs_gemm", "oracle_mx_gemm"):
+        for name in ("oracle_bs_gemm", "oracle_mx_gemm", "oracle_pt_gemm"):
             fn = getattr(lib, name)
             fn.restype = None
             fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -142,6 +144,22 @@ class Oracle:
         if a_e8m0.shape != (M, K // 32) or b_e8m0.shape != (N, K // 32):
             raise ValueError("bad scale shape")
         return self._run(self.lib.oracle_mx_gemm, A, a_e8m0, B, b_e8m0, M, N, K, rows, cols)
+
+
+    def pt_gemm(self, A, a_scale, B, b_scale, rows=None, cols=None):
+        """Route PT (promote-free twin). A [M,K], B [N,K] uint8 e4m3 codes; a_scale [M] and
+        b_scale [N] fp32 (one per row of A / of B). Returns (fp64 values, bf16 bits)."""
+        A = np.ascontiguousarray(A, dtype=np.uint8)
+        B = np.ascontiguousarray(B, dtype=np.uint8)
+        M, K = A.shape
+        N = B.shape[0]
+        if B.shape[1] != K:
+            raise ValueError("bad K")
+        a_scale = np.ascontiguousarray(a_scale, dtype=np.float32).reshape(-1)
+        b_scale = np.ascontiguousarray(b_scale, dtype=np.float32).reshape(-1)
+        if a_scale.shape != (M,) or b_scale.shape != (N,):
+            raise ValueError("bad scale shape")
+        return self._run(self.lib.oracle_pt_gemm, A, a_scale, B, b_scale, M, N, K, rows, cols)
 
 
 _default: Oracle | None = None

@@ -16,6 +16,10 @@
  *   scales are exact powers of two applied per 32-wide K group):
  *       C[m,n] = bf16( sum_g 2^(ea[m,g]-127) * 2^(eb[n,g]-127) * sum_{k in group g} A[m,k]*B[n,k] )
  *
+ *   route PT (the promote-free twin, see oracle_pt_gemm): one fp32 scale per row of A and
+ *   one per row of B:
+ *       C[m,n] = bf16( a_s[m] * b_s[n] * sum_k A[m,k]*B[n,k] )
+ *
  * Precision: every e4m3 value is an integer times 2^-9, so every product is an integer
  * times 2^-18 below 2^36 and a 128-term block sum stays below 2^43: the block sums are
  * exact in fp64. The scale product a_s*b_s (24+24 significant bits) is exact in fp64.
@@ -163,6 +167,47 @@ void oracle_mx_gemm(const uint8_t *A, const uint8_t *a_e8m0, const uint8_t *B,
                 acc += p * e8m0_decode(a_e8m0[(size_t)m * G + g]) *
                        e8m0_decode(b_e8m0[(size_t)n * G + g]);
             }
+            if (out_acc)
+                out_acc[(size_t)i * nc + j] = acc;
+            if (out_bf16)
+                out_bf16[(size_t)i * nc + j] = bf16_round_from_f64(acc);
+        }
+        free(arow);
+    }
+}
+
+/* Route PT, the promote-free twin of route BS (page "Flydsl Fp8 Blockscale Gemm",
+ * Bottleneck diagnosis, item 2: the same matrix work with a cheap row-by-column scale in
+ * place of the per-block promote; page "aiter PR #6370" calls the per-token / per-channel
+ * kernel "ptpc"):
+ *   A [M, K] e4m3 codes, a_scale [M] fp32 (one per row of A, per token)
+ *   B [N, K] e4m3 codes, b_scale [N] fp32 (one per row of B, per output channel)
+ *       C[m,n] = bf16( a_s[m] * b_s[n] * sum_k A[m,k]*B[n,k] )
+ * The dot product is exact in fp64 while K <= 2^17 (each product is an integer times 2^-18
+ * below 2^36), a_s*b_s is exact, and their product rounds once before the bf16 rounding.
+ * Same output convention as oracle_bs_gemm. */
+void oracle_pt_gemm(const uint8_t *A, const float *a_scale, const uint8_t *B,
+                    const float *b_scale, int M, int N, int K, const int *rows, int nr,
+                    const int *cols, int nc, double *out_acc, uint16_t *out_bf16)
+{
+    double table[256];
+    (void)M;
+    (void)N;
+    for (int c = 0; c < 256; c++)
+        table[c] = e4m3_decode((uint8_t)c);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < nr; i++) {
+        const int m = rows[i];
+        double *arow = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+        for (int k = 0; k < K; k++)
+            arow[k] = table[A[(size_t)m * K + k]];
+        for (int j = 0; j < nc; j++) {
+            const int n = cols[j];
+            const uint8_t *brow = B + (size_t)n * K;
+            double dot = 0.0;
+            for (int k = 0; k < K; k++)
+                dot += arow[k] * table[brow[k]];
+            const double acc = dot * ((double)a_scale[m] * (double)b_scale[n]);
             if (out_acc)
                 out_acc[(size_t)i * nc + j] = acc;
             if (out_bf16)

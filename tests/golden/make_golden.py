@@ -1,5 +1,5 @@
 """Writes tests/golden/*.txt: regression fixtures of the oracle's output on the seeded
-128x256x512 workloads (route BS and route MX). Calls only the oracle and the input
+128x256x512 workloads (route BS, route MX and the promote-free twin, route PT). Calls only the oracle and the input
 generator. The pages print no worked numeric example, so these fixtures pin the oracle
 against its own earlier, pinned self (they catch accidental changes), nothing more.
 
@@ -39,6 +39,10 @@ def main():
     acc, bits = o.mx_gemm(y.A, y.a_e8m0, y.B, y.b_e8m0)
     write("tiny_mx_seed0.txt", bits, acc,
           "oracle route MX, M=128 N=256 K=512 seed 0 (workload.mx_inputs); columns: m n bf16 fp64")
+    z = workload.pt_inputs(128, 256, 512, 0)
+    acc, bits = o.pt_gemm(z.A, z.a_scale, z.B, z.b_scale)
+    write("tiny_pt_seed0.txt", bits, acc,
+          "oracle route PT, M=128 N=256 K=512 seed 0 (workload.pt_inputs); columns: m n bf16 fp64")
 
 
 if __name__ == "__main__":

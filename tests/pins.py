@@ -428,10 +428,105 @@ def pin_invariant_mx_unit_and_lossless(o, seed=11):
     assert np.array_equal(f(bits2), 2 * f(bits1))
 
 
+def exact_pt(A, a_scale, B, b_scale):
+    """Exact route-PT result as Fractions [M][N] plus |value| (one rounding in the oracle)."""
+    ai = e4m3_int(A)
+    bi = e4m3_int(B)
+    dots = ai @ bi.T  # int64, exact (|dot| < K * 2^36)
+    M, N = dots.shape
+    two18 = Fraction(1, 2 ** 18)
+    sa = [Fraction(float(v)) for v in a_scale]
+    sb = [Fraction(float(v)) for v in b_scale]
+    out = [[int(dots[m, n]) * two18 * sa[m] * sb[n] for n in range(N)] for m in range(M)]
+    mag = [[abs(v) for v in row] for row in out]
+    return out, mag
+
+
+def pin_pt_brute_force(o, seed=12, M=5, N=70, K=384):
+    """Route PT on random codes (with specials) and random fp32 row scales equals the exact
+    brute force (a single rounding before the bf16 one)."""
+    rng = np.random.default_rng(seed)
+    A = special_codes(rng, (M, K))
+    B = special_codes(rng, (N, K))
+    sa = random_fp32_scales(rng, (M,))
+    sb = random_fp32_scales(rng, (N,))
+    acc, bits = o.pt_gemm(A, sa, B, sb)
+    exact, mag = exact_pt(A, sa, B, sb)
+    compare_exact(acc, bits, exact, mag, 1)
+
+
+def pin_pt_inputs_exact(o, seed=0):
+    """A seeded per-token / per-channel quantised 64x96x512 problem equals the exact brute
+    force."""
+    x = workload.pt_inputs(64, 96, 512, seed)
+    acc, bits = o.pt_gemm(x.A, x.a_scale, x.B, x.b_scale)
+    exact, mag = exact_pt(x.A, x.a_scale, x.B, x.b_scale)
+    compare_exact(acc, bits, exact, mag, 1)
+
+
+def pin_pt_closed_form_integers(o, seed=13):
+    """Integer-valued codes with scales 2 (rows of A) and 1/2 (rows of B): C is the int64
+    matmul, rounded to bf16 by torch (fp32-exact)."""
+    rng = np.random.default_rng(seed)
+    ints = rng.integers(-4, 5, size=(9, 384))
+    intb = rng.integers(-4, 5, size=(40, 384))
+    A = workload.e4m3_encode(ints.astype(np.float32))
+    B = workload.e4m3_encode(intb.astype(np.float32))
+    acc, bits = o.pt_gemm(A, np.full(9, 2.0, np.float32), B, np.full(40, 0.5, np.float32))
+    ref = ints @ intb.T
+    assert np.array_equal(acc, ref.astype(np.float64))
+    want = torch.from_numpy(ref.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(bits, want)
+
+
+def pin_pt_cross_route_bs(o, seed=14):
+    """PT with power-of-two row scales, the weight scales constant inside each 128-row block,
+    equals route BS with those scales broadcast over the K blocks, bit for bit (every term is
+    then exact in both)."""
+    rng = np.random.default_rng(seed)
+    M, N, K = 6, 256, 512
+    A = special_codes(rng, (M, K))
+    B = special_codes(rng, (N, K))
+    ea = rng.integers(110, 140, size=M)
+    eb = rng.integers(110, 140, size=N // 128)
+    sa = np.exp2(ea - 127.0).astype(np.float32)
+    sb_blocks = np.exp2(eb - 127.0).astype(np.float32)
+    sb = np.repeat(sb_blocks, 128)
+    acc, bits = o.pt_gemm(A, sa, B, sb)
+    KB = K // 128
+    acc2, bits2 = o.bs_gemm(A, np.repeat(sa[:, None], KB, axis=1), B, np.repeat(sb_blocks[:, None], KB, axis=1))
+    assert np.array_equal(acc, acc2) and np.array_equal(bits, bits2)
+
+
+def pin_pt_scale_linearity(o, seed=15):
+    """Scaling a_s[m] or b_s[n] by a power of two scales exactly that row or column of C
+    (bitwise, away from overflow); the other outputs are unchanged."""
+    rng = np.random.default_rng(seed)
+    M, N, K = 6, 50, 256
+    A = special_codes(rng, (M, K))
+    B = special_codes(rng, (N, K))
+    sa = random_fp32_scales(rng, (M,))
+    sb = random_fp32_scales(rng, (N,))
+    acc, bits = o.pt_gemm(A, sa, B, sb)
+    sa2 = sa.copy()
+    sa2[2] *= 4
+    sb2 = sb.copy()
+    sb2[7] *= 0.5
+    acc2, bits2 = o.pt_gemm(A, sa2, B, sb2)
+    f = lambda b: (b.astype(np.uint32) << 16).view(np.float32)
+    expect = f(bits).copy()
+    expect[2, :] *= 4
+    expect[:, 7] *= 0.5
+    assert np.array_equal(f(bits2), expect)
+    assert np.array_equal(acc2[np.ix_([0, 1, 3, 4, 5], [c for c in range(N) if c != 7])],
+                          acc[np.ix_([0, 1, 3, 4, 5], [c for c in range(N) if c != 7])])
+
+
 ALL_PINS = [
     pin_e4m3_decode, pin_e8m0_decode, pin_bf16_round_fp32_exact, pin_bf16_round_exact,
     pin_bs_brute_force, pin_bs_tiny_config_exact, pin_mx_brute_force, pin_closed_form_ones,
     pin_closed_form_integers, pin_closed_form_one_hot, pin_closed_form_pow2_block_scales,
     pin_invariant_scale_doubling, pin_invariant_permutations, pin_invariant_zero_block,
-    pin_invariant_cross_route, pin_invariant_mx_unit_and_lossless,
+    pin_invariant_cross_route, pin_invariant_mx_unit_and_lossless, pin_pt_brute_force,
+    pin_pt_inputs_exact, pin_pt_closed_form_integers, pin_pt_cross_route_bs, pin_pt_scale_linearity,
 ]

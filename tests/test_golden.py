@@ -18,11 +18,14 @@ def _read(name):
     return digest, picks
 
 
-@pytest.mark.parametrize("route", ["bs", "mx"])
+@pytest.mark.parametrize("route", ["bs", "mx", "pt"])
 def test_golden_tiny(oracle, route):
     if route == "bs":
         x = workload.bs_inputs(128, 256, 512, 0)
         acc, bits = oracle.bs_gemm(x.A, x.a_scale, x.B, x.b_scale)
+    elif route == "pt":
+        z = workload.pt_inputs(128, 256, 512, 0)
+        acc, bits = oracle.pt_gemm(z.A, z.a_scale, z.B, z.b_scale)
     else:
         y = workload.mx_inputs(128, 256, 512, 0)
         acc, bits = oracle.mx_gemm(y.A, y.a_e8m0, y.B, y.b_e8m0)

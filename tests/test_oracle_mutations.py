@@ -25,6 +25,9 @@ MUTATIONS = {
     "mx_a_scale_for_b": ("e8m0_decode(b_e8m0[(size_t)n * G + g])", "e8m0_decode(a_e8m0[(size_t)m * G + g])"),
     "block_boundary": ("k < kb * 128 + 128", "k < kb * 128 + 127"),
     "mx_group_boundary": ("k < g * 32 + 32", "k < g * 32 + 31"),
+    "pt_b_scale_by_row": ("(double)a_scale[m] * (double)b_scale[n]", "(double)a_scale[m] * (double)b_scale[m]"),
+    "pt_b_scale_dropped": ("dot * ((double)a_scale[m] * (double)b_scale[n])", "dot * (double)a_scale[m]"),
+    "pt_last_k_dropped": ("for (int k = 0; k < K; k++)\n                dot +=", "for (int k = 0; k < K - 1; k++)\n                dot +="),
 }
 
 

@@ -142,6 +142,23 @@ def mx_inputs(M: int, N: int, K: int, seed: int = 0) -> MXInputs:
     return MXInputs(M, N, K, qa, ea, qb, eb)
 
 
+@dataclass
+class PTInputs:
+    """Route PT: one fp32 scale per row of A (per token) and per row of B (per channel)."""
+    A: np.ndarray        # [M, K] uint8 e4m3 codes
+    a_scale: np.ndarray  # [M] fp32
+    B: np.ndarray        # [N, K] uint8 e4m3 codes
+    b_scale: np.ndarray  # [N] fp32
+
+
+def pt_inputs(M: int, N: int, K: int, seed: int = 0) -> PTInputs:
+    """Route-PT operands: A and B quantised per whole row with fp32 scale amax/448."""
+    a, b = draw(M, N, K, seed)
+    A, sa = quantize_groups_fp32(a, 1, K)
+    B, sb = quantize_groups_fp32(b, 1, K)
+    return PTInputs(A, np.ascontiguousarray(sa.reshape(M)), B, np.ascontiguousarray(sb.reshape(N)))
+
+
 def sample_indices(n_total: int, n_pick: int, seed: int) -> np.ndarray:
     """A seeded, sorted sample of distinct indices that always includes the first and last."""
     if n_pick >= n_total:

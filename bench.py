@@ -15,6 +15,9 @@ every input already resident in HBM. Prints ONE JSON line on stdout:
                   (tiny, narrow-N, K-light, wide-N, mxfp8), TFLOP/s, % of peak, algorithmic
                   HBM GB/s, and the "cold" time of single launches that each follow a 1 GiB
                   write evicting L2 and the MALL
+  ceiling_twin -- the promote-free twin (fp8pt_gemm: one scale per row of A and of B, applied
+                  in the epilogue) on the route-BS shapes: the same matrix work without the
+                  per-block promote; bs_over_twin is the promote's cost as a time ratio
   cpu_baseline -- the CPU oracle (fp64, OpenMP) on a bounded sample of output rows
   parity       -- sampled rows/columns of the timed output against the oracle
 
@@ -75,18 +78,25 @@ def algorithmic_bytes(route: str, M: int, N: int, K: int) -> int:
 class Case:
     """Device-resident operands of one workload plus a launch closure on a given stream."""
 
-    def __init__(self, name: str, seed: int, stream):
+    def __init__(self, name: str, seed: int, stream, twin: bool = False):
         import torch
 
         import fp8_block_scaled_e4m3_amd as fb
         import workload
 
         cfg = workload.CONFIGS[name]
-        self.name, self.route = name, cfg["route"]
+        self.name, self.route = name, ("pt" if twin else cfg["route"])
         self.M, self.N, self.K = cfg["M"], cfg["N"], cfg["K"]
         dev = torch.device("cuda:0")
         t0 = time.time()
-        if self.route == "bs":
+        if self.route == "pt":
+            z = workload.pt_inputs(self.M, self.N, self.K, seed)
+            self.host = z
+            self.A = torch.from_numpy(z.A).to(dev)
+            self.sa = torch.from_numpy(z.a_scale).to(dev)
+            self.B = fb.prep_weights(torch.from_numpy(z.B).to(dev), stream)
+            self.sb = torch.from_numpy(z.b_scale).to(dev)
+        elif self.route == "bs":
             x = workload.bs_inputs(self.M, self.N, self.K, seed)
             self.host = x
             self.A = torch.from_numpy(x.A).to(dev)
@@ -103,10 +113,10 @@ class Case:
         self.C = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
         log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s")
-        fn = fb.fp8bs_gemm if self.route == "bs" else fb.fp8mx_gemm
+        fn = {"bs": fb.fp8bs_gemm, "mx": fb.fp8mx_gemm, "pt": fb.fp8pt_gemm}[self.route]
         self.launch = lambda: fn(self.A, self.sa, self.B, self.sb, self.C, stream)
-        self.config = fb.fp8bs_select_config(fb.ROUTE_BS if self.route == "bs" else fb.ROUTE_MX,
-                                             self.M, self.N, self.K).as_dict()
+        route_id = {"bs": fb.ROUTE_BS, "mx": fb.ROUTE_MX, "pt": fb.ROUTE_PT}[self.route]
+        self.config = fb.fp8bs_select_config(route_id, self.M, self.N, self.K).as_dict()
 
     @property
     def flops(self) -> int:
@@ -390,6 +400,21 @@ def main() -> int:
                 torch.cuda.empty_cache()
             per_shape[name] = row
 
+        # the promote-free twin (route PT) on the route-BS shapes: same matrix work, scales
+        # applied once in the epilogue -- the cost of the per-block promote is the difference
+        twin = {}
+        for name in [n for n in names if workload.CONFIGS[n]["route"] == "bs" and n != "tiny"]:
+            tc = Case(name, 0, stream, twin=True)
+            _, ev, steps = tc.steady_state(stream)
+            bs_us = per_shape[name]["us"]
+            twin[name] = dict(us=round(ev * 1e6, 2), tflops=round(tc.flops / ev / 1e12, 1),
+                              pct_peak=round(100 * tc.flops / ev / 1e12 / PEAK_FP8_TFLOPS, 2),
+                              bs_over_twin=round(bs_us / (ev * 1e6), 3), config=tc.config)
+            log(f"[bench] twin {name}: {twin[name]}")
+            tc.free()
+            del tc
+            torch.cuda.empty_cache()
+
     case = main_row["case"]
     value = case.flops / main_row["wall"] / 1e12
     achieved = case.flops / main_row["ev"] / 1e12
@@ -417,6 +442,7 @@ def main() -> int:
         "mfma_ceiling": main_row["ceiling"],
         "cpu_baseline": main_row["baseline"],
         "per_shape": per_shape,
+        "ceiling_twin": twin,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "kernel_source_sha256": kernel_source_hash()[:16]},
     }

@@ -11,6 +11,8 @@ Routes (see include/fp8bs.h for layouts and constraints):
   (``a_scale`` laid out [K/128, M]) and fp32 per-128x128 weight scales ([N/128, K/128]).
 * ``fp8mx_gemm(A, a_scale_packed, B_prep, b_scale_packed, C)`` -- 1x32 ue8m0 scales, packed
   once by ``fp8mx_pack_a_scale`` / ``fp8mx_prep_weights``.
+* ``fp8pt_gemm(A, a_scale, B_prep, b_scale, C)`` -- the promote-free twin: fp32 ``a_scale`` [M]
+  and ``b_scale`` [N], applied once in the epilogue.
 """
 from __future__ import annotations
 
@@ -25,7 +27,7 @@ __all__ = [
     "fp8mx_packed_scale_bytes", "fp8mx_pack_a_scale", "fp8mx_prep_weights", "fp8mx_gemm",
     "prep_weights", "mx_prep_weights", "mx_pack_a_scale",
     "Config", "ROUTE_BS", "ROUTE_MX", "fp8bs_select_config", "fp8bs_gemm_with_config", "fp8mx_gemm_with_config",
-    "fp8bs_mfma_ceiling",
+    "fp8bs_mfma_ceiling", "ROUTE_PT", "fp8pt_gemm", "fp8pt_gemm_with_config",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -47,9 +49,11 @@ SIGNATURES = {
     "fp8bs_gemm_with_config": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp, _vp]),
     "fp8mx_gemm_with_config": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp, _vp]),
     "fp8bs_mfma_ceiling": (_int, [_vp, _vp, _int, _int, _int, _int, _vp, _int, _vp, _vp]),
+    "fp8pt_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp]),
+    "fp8pt_gemm_with_config": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp, _vp]),
 }
 
-ROUTE_BS, ROUTE_MX = 0, 1
+ROUTE_BS, ROUTE_MX, ROUTE_PT = 0, 1, 2
 
 
 class Config(ctypes.Structure):
@@ -163,6 +167,26 @@ def fp8mx_gemm(A: torch.Tensor, a_scale_packed: torch.Tensor, B_prep: torch.Tens
     N = C.shape[1]
     _check("fp8mx_gemm", lib.fp8mx_gemm(_ptr(A), _ptr(a_scale_packed), _ptr(B_prep), _ptr(b_scale_packed),
                                         _ptr(C), M, N, K, _stream(stream)))
+    return C
+
+
+def fp8pt_gemm(A: torch.Tensor, a_scale: torch.Tensor, B_prep: torch.Tensor, b_scale: torch.Tensor,
+               C: torch.Tensor, stream=None) -> torch.Tensor:
+    """Route PT (promote-free twin): C[M,N] (bf16) = a_scale[m] * b_scale[n] * (A B^T)[m,n] with
+    A [M,K] uint8 e4m3 codes, a_scale [M] fp32, B_prep from fp8bs_prep_weights, b_scale [N] fp32."""
+    M, K = A.shape
+    N = C.shape[1]
+    _check("fp8pt_gemm", lib.fp8pt_gemm(_ptr(A), _ptr(a_scale), _ptr(B_prep), _ptr(b_scale), _ptr(C),
+                                        M, N, K, _stream(stream)))
+    return C
+
+
+def fp8pt_gemm_with_config(A, a_scale, B_prep, b_scale, C, config: Config, stream=None):
+    M, K = A.shape
+    N = C.shape[1]
+    _check("fp8pt_gemm_with_config",
+           lib.fp8pt_gemm_with_config(_ptr(A), _ptr(a_scale), _ptr(B_prep), _ptr(b_scale), _ptr(C), M, N, K,
+                                      ctypes.byref(config), _stream(stream)))
     return C
 
 

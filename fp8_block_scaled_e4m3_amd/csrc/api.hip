@@ -37,6 +37,15 @@ int check_mx_shape(int M, int N, int K)
     return FP8BS_OK;
 }
 
+// Shape rules of route PT: weight rows in whole 64-row windows of the prepared order, K in
+// whole 128-wide steps; any M (the last row tile masks its stores).
+int check_pt_shape(int M, int N, int K)
+{
+    if (M < 0 || N < 64 || N % 64 != 0 || K < 128 || K % 128 != 0 || !fits_offsets(M, N, K))
+        return FP8BS_E_SHAPE;
+    return FP8BS_OK;
+}
+
 int find_variant(const fp8bs_config& c)
 {
     for (int v = 0;; ++v) {
@@ -86,7 +95,7 @@ fp8bs_config select(int route, int M, int N, int K)
         const int xcd = group_m * (N / block_n) <= 2 * kCUs ? 1 : 2;
         return make_config(variant, group_m, xcd, 1);
     };
-    if (route == fp8bs::kRouteMX && N % 128 != 0)
+    if ((route == fp8bs::kRouteMX || route == fp8bs::kRoutePT) && N % 128 != 0)
         return cfg(7, 64);
     if (N % 256 == 0 && tiles(256, 256) >= 2 * kCUs)
         return cfg(2, 256);
@@ -155,6 +164,22 @@ int check_mx_args(const void* A, const void* a_scale_packed, const void* B_prep,
     return FP8BS_OK;
 }
 
+int check_pt_args(const void* A, const float* a_scale, const void* B_prep, const float* b_scale, void* C,
+                  int M, int N, int K)
+{
+    int st = check_pt_shape(M, N, K);
+    if (st != FP8BS_OK)
+        return st;
+    if (M == 0)
+        return -1;
+    if (!A || !a_scale || !B_prep || !b_scale || !C)
+        return FP8BS_E_NULL;
+    if (!aligned(A, 16) || !aligned(B_prep, 16) || !aligned(C, 16) || !aligned(a_scale, 4) ||
+        !aligned(b_scale, 16))
+        return FP8BS_E_ALIGN;
+    return FP8BS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -196,9 +221,11 @@ int fp8bs_select_config(int route, int M, int N, int K, fp8bs_config* out)
 {
     if (!out)
         return FP8BS_E_NULL;
-    if (route != FP8BS_ROUTE_BS && route != FP8BS_ROUTE_MX)
+    if (route != FP8BS_ROUTE_BS && route != FP8BS_ROUTE_MX && route != FP8BS_ROUTE_PT)
         return FP8BS_E_CONFIG;
-    int st = route == FP8BS_ROUTE_BS ? check_bs_shape(M, N, K) : check_mx_shape(M, N, K);
+    int st = route == FP8BS_ROUTE_BS   ? check_bs_shape(M, N, K)
+             : route == FP8BS_ROUTE_MX ? check_mx_shape(M, N, K)
+                                       : check_pt_shape(M, N, K);
     if (st != FP8BS_OK)
         return st;
     *out = select(route, M, N, K);
@@ -277,6 +304,25 @@ int fp8mx_gemm_with_config(const void* A, const void* a_scale_packed, const void
     if (st != FP8BS_OK)
         return st < 0 ? FP8BS_OK : st;
     return run(fp8bs::kRouteMX, A, a_scale_packed, B_prep, b_scale_packed, C, M, N, K, config, stream);
+}
+
+int fp8pt_gemm(const void* A, const float* a_scale, const void* B_prep, const float* b_scale, void* C,
+               int M, int N, int K, hipStream_t stream)
+{
+    int st = check_pt_args(A, a_scale, B_prep, b_scale, C, M, N, K);
+    if (st != FP8BS_OK)
+        return st < 0 ? FP8BS_OK : st;
+    const fp8bs_config cfg = select(fp8bs::kRoutePT, M, N, K);
+    return run(fp8bs::kRoutePT, A, a_scale, B_prep, b_scale, C, M, N, K, &cfg, stream);
+}
+
+int fp8pt_gemm_with_config(const void* A, const float* a_scale, const void* B_prep, const float* b_scale,
+                           void* C, int M, int N, int K, const fp8bs_config* config, hipStream_t stream)
+{
+    int st = check_pt_args(A, a_scale, B_prep, b_scale, C, M, N, K);
+    if (st != FP8BS_OK)
+        return st < 0 ? FP8BS_OK : st;
+    return run(fp8bs::kRoutePT, A, a_scale, B_prep, b_scale, C, M, N, K, config, stream);
 }
 
 int fp8bs_mfma_ceiling(const void* A, const void* B_prep, int M, int N, int K, int iters, float* sink, int sink_len,

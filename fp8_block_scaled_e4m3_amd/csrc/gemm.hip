@@ -62,20 +62,24 @@ struct Tile {
     static constexpr int SJ = TN / 16;
     static constexpr int kABytes = BM * 128;
     static constexpr int kBBytes = BN * 128;
-    static constexpr int kSABytes = BM * 4;                           // fp32 per row / packed dword per row
-    static constexpr int kSBBytes = ROUTE == kRouteBS ? 256 : BN * 4;  // BS: <= 64 weight-block scales
+    // per-step scales in LDS: BS fp32 per row of A and <= 64 weight-block scales; MX one packed
+    // dword per row of each operand; PT none (its scales are applied once, in the epilogue)
+    static constexpr int kSABytes = ROUTE == kRoutePT ? 0 : BM * 4;
+    static constexpr int kSBBytes = ROUTE == kRoutePT ? 0 : ROUTE == kRouteBS ? 256 : BN * 4;
     static constexpr int kStageBytes = kABytes + kBBytes + kSABytes + kSBBytes;
     static constexpr int kLoadsA = BM / 8 / kWaves;  // 1 KB (8-row) loads per wave per step
     static constexpr int kLoadsB = BN / 8 / kWaves;
-    static constexpr int kScaleLoadsA = BM / 64;     // 256-byte loads
-    static constexpr int kScaleLoadsB = ROUTE == kRouteBS ? 1 : BN / 64;
+    static constexpr int kScaleLoadsA = ROUTE == kRoutePT ? 0 : BM / 64;  // 256-byte loads
+    static constexpr int kScaleLoadsB = ROUTE == kRoutePT ? 0 : ROUTE == kRouteBS ? 1 : BN / 64;
     static constexpr int kScaleLoads = kScaleLoadsA + kScaleLoadsB;
     static constexpr int kLoadsS = (kScaleLoads + kWaves - 1) / kWaves;
     static constexpr int kLoadsPerStep = kLoadsA + kLoadsB + kLoadsS;
     static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "whole 8-row groups per wave");
     static_assert(BM % 64 == 0 && TM % 16 == 0 && TN % 64 == 0, "16x16 sub-tiles, 64-row scale loads, "
                   "whole 64-column windows of the prepared weight order per wave");
-    static_assert(ROUTE == kRouteMX ? (TM % 64 == 0 && TN % 64 == 0) : (TN <= 128 && 128 % TN == 0),
+    static_assert(ROUTE == kRouteMX   ? (TM % 64 == 0 && TN % 64 == 0)
+                  : ROUTE == kRouteBS ? (TN <= 128 && 128 % TN == 0)
+                                      : true,
                   "MX: whole 64-row packed scale groups; BS: a wave's columns in one weight-scale block");
     static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
     static_assert(STAGES * kStageBytes <= kLdsCapacity, "LDS capacity");
@@ -206,8 +210,8 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     // holds logical K chunk (l&7) ^ swz(row); rows past M re-read row M-1 (never stored).
     uint32_t voffA[T::kLoadsA];
     uint32_t voffB[T::kLoadsB];
-    uint32_t voffS[T::kLoadsS];  // scale loads: byte offset without the K-block term
-    uint32_t kstrS[T::kLoadsS];  // bytes per K block of that scale array
+    uint32_t voffS[T::kLoadsS > 0 ? T::kLoadsS : 1];  // scale loads: byte offset without the K-block term
+    uint32_t kstrS[T::kLoadsS > 0 ? T::kLoadsS : 1];  // bytes per K block of that scale array
     int load_tile = -1;          // tile index (in this workgroup's list) the descriptors describe
     auto setup_loads = [&](int i) {
         int tm, tn;
@@ -328,6 +332,27 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
         tile_of((int)blockIdx.x + i * grid, grid, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
         const int mbase = tm * BM + wm * T::TM + frow;
         const int nbase = tn * BN + wn * T::TN + 8 * (int)q;
+        // Route PT: C = acc * (a_s[m] * b_s[n]), with the row and column scales read here, once
+        // per tile, before any store of the tile, and waited for at once (the empty asm uses):
+        // no store then sits between a scale load and its use.
+        float rs[ROUTE == kRoutePT ? T::SI : 1];
+        v4f cs[ROUTE == kRoutePT ? T::SJ : 1];
+        if constexpr (ROUTE == kRoutePT) {
+            const float* as = (const float*)a_scale;
+            const float* bs = (const float*)b_scale;
+#pragma unroll
+            for (int si = 0; si < T::SI; ++si)
+                rs[si] = as[min(mbase + 16 * si, M - 1)];
+#pragma unroll
+            for (int sj = 0; sj < T::SJ; ++sj)
+                cs[sj] = *(const v4f*)(bs + nbase + 32 * (sj >> 1) + 4 * (sj & 1));
+#pragma unroll
+            for (int si = 0; si < T::SI; ++si)
+                asm volatile("" : "+v"(rs[si]));
+#pragma unroll
+            for (int sj = 0; sj < T::SJ; ++sj)
+                asm volatile("" : "+v"(cs[sj]));
+        }
 #pragma unroll
         for (int si = 0; si < T::SI; ++si) {
             const int m = mbase + 16 * si;
@@ -335,8 +360,12 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
                 uint16_t* crow = C + (size_t)m * N + nbase;
 #pragma unroll
                 for (int sj = 0; sj < T::SJ; sj += 2) {
-                    const v4f lo = acc[si][sj];
-                    const v4f hi = acc[si][sj + 1];
+                    v4f lo = acc[si][sj];
+                    v4f hi = acc[si][sj + 1];
+                    if constexpr (ROUTE == kRoutePT) {
+                        lo = lo * (cs[sj] * rs[si]);
+                        hi = hi * (cs[sj + 1] * rs[si]);
+                    }
                     v4i packed;
                     packed.x = (int)pack_bf16x2(lo.x, lo.y);
                     packed.y = (int)pack_bf16x2(lo.z, lo.w);
@@ -390,7 +419,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
             for (int i = 0; i < T::SI; ++i)
                 F.sa[i] = sa[16 * i];
             F.sb = ((const float*)(sS + T::kSABytes))[(wn * T::TN) >> 7];
-        } else {
+        } else if constexpr (ROUTE == kRouteMX) {
 #pragma unroll
             for (int g = 0; g < GA; ++g)
                 F.ia[g] = ((const int*)sS)[(wm * T::TM / 64 + g) * 64 + lane];
@@ -422,6 +451,8 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
                     p[t % 3] = mfma_f8(F.b[j], F.a[i], v4f{0.f, 0.f, 0.f, 0.f});
                     if constexpr (t >= 2)
                         promote(std::integral_constant<int, t - 2>{});
+                } else if constexpr (ROUTE == kRoutePT) {
+                    acc[i][j] = mfma_f8(F.b[j], F.a[i], acc[i][j]);
                 } else {
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                         F.b[j], F.a[i], acc[i][j], kFmtE4M3, kFmtE4M3, j & 3, F.ib[j / 4], i & 3, F.ia[i / 4]);
@@ -553,7 +584,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
             for (int i = 0; i < T::SI; ++i)
                 sa_r[i] = sa[16 * i];
             sb_r = ((const float*)(sS + T::kSABytes))[(wn * T::TN) >> 7];
-        } else {
+        } else if constexpr (ROUTE == kRouteMX) {
 #pragma unroll
             for (int g = 0; g < GA; ++g)
                 ia[g] = ((const int*)sS)[(wm * T::TM / 64 + g) * 64 + lane];
@@ -607,6 +638,9 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
                     p[t % 3] = mfma_f8(b, a, v4f{0.f, 0.f, 0.f, 0.f});
                     if constexpr (t >= 2)
                         promote(std::integral_constant<int, t - 2>{});
+                } else if constexpr (ROUTE == kRoutePT) {
+                    // one unscaled accumulation over all of K; the scales come in the epilogue
+                    acc[i][j] = mfma_f8(b, a, acc[i][j]);
                 } else {
                     // weights first: the weight scale byte of sub-tile j, the activation byte of row i
                     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -797,6 +831,8 @@ static hipError_t launch_variant(int route, const GemmArgs& a, const GemmConfig&
         else
             return hipErrorInvalidValue;
     }
+    if (route == kRoutePT)
+        return launch_tile<kRoutePT, BM, BN, WM, WN, ST, PP>(a, c);
     if constexpr (mx_fits<BM, BN, WM, WN, ST>())
         return launch_tile<kRouteMX, BM, BN, WM, WN, ST, PP>(a, c);
     else
@@ -811,6 +847,8 @@ bool variant_supports(int route, int v)
     const int TM = vi->block_m / vi->waves_m, TN = vi->block_n / vi->waves_n;
     if (route == kRouteBS)
         return TN <= 128 && 128 % TN == 0;
+    if (route == kRoutePT)
+        return true;
     return TM % 64 == 0 && TN % 64 == 0 && vi->stages * (vi->block_m * 132 + vi->block_n * 132) <= kLdsCapacity;
 }
 

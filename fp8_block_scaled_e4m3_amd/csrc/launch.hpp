@@ -6,7 +6,7 @@
 
 namespace fp8bs {
 
-enum { kRouteBS = 0, kRouteMX = 1 };
+enum { kRouteBS = 0, kRouteMX = 1, kRoutePT = 2 };
 
 struct GemmArgs {
     const void* A;        // [M, K] e4m3

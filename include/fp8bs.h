@@ -17,6 +17,14 @@
  *               C[m,n] = bf16( sum_g 2^(ea[m,g]-127) * 2^(eb[n,g]-127) * sum_{k in g} A[m,k]*B[n,k] )
  *             (page "aiter PR #6370", "Why it is faster").
  *
+ *   route PT  fp8pt_gemm: the promote-free twin of route BS, one fp32 scale per row of A and per
+ *             row of B (per token / per output channel):
+ *               C[m,n] = bf16( a_s[m] * b_s[n] * sum_k A[m,k]*B[n,k] )
+ *             The same matrix-core work as route BS with the scales applied once, in the
+ *             epilogue: the instrument that separates the cost of the per-block promote from
+ *             the rest of the kernel (page "Flydsl Fp8 Blockscale Gemm", Bottleneck diagnosis,
+ *             item 2; page "aiter PR #6370" calls such a kernel "ptpc").
+ *
  * Conventions shared by every entry point:
  *   - Pointers are device pointers unless stated otherwise; the caller owns every buffer.
  *     The library never allocates, frees or keeps per-call state.
@@ -114,6 +122,21 @@ int fp8mx_gemm(const void *A, const void *a_scale_packed, const void *B_prep,
                const void *b_scale_packed, void *C, int M, int N, int K, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Route PT.
+ * ------------------------------------------------------------------------------------------ */
+
+/* C[M,N] = bf16(a_s[m] * b_s[n] * (A B^T)[m,n]).
+ *   A        [M, K] e4m3, row-major.
+ *   a_scale  [M] fp32: a_scale[m] scales row m of A.
+ *   B_prep   the output of fp8bs_prep_weights for B [N, K] (the same buffer route BS uses).
+ *   b_scale  [N] fp32: b_scale[n] scales row n of B (output column n).
+ *   C        [M, N] bf16, row-major; every element is written.
+ * Constraints: M >= 0 (M == 0 is a no-op), N % 64 == 0, N >= 64, K % 128 == 0, K >= 128;
+ * A, B_prep, C and b_scale 16-byte aligned, a_scale 4-byte aligned. */
+int fp8pt_gemm(const void *A, const float *a_scale, const void *B_prep, const float *b_scale,
+               void *C, int M, int N, int K, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * Kernel configuration (introspection and ablation). The plain entry points pick a
  * configuration from (M, N, K) alone (page "Flydsl Fp8 Blockscale Gemm", Per-shape recipes:
  * selection by shape, never by layer name); the *_with_config entry points run an explicit one
@@ -121,7 +144,7 @@ int fp8mx_gemm(const void *A, const void *a_scale_packed, const void *B_prep,
  * Bottleneck diagnosis: ablation is the ground truth).
  * ------------------------------------------------------------------------------------------ */
 
-enum { FP8BS_ROUTE_BS = 0, FP8BS_ROUTE_MX = 1 };
+enum { FP8BS_ROUTE_BS = 0, FP8BS_ROUTE_MX = 1, FP8BS_ROUTE_PT = 2 };
 
 typedef struct {
     int block_m;     /* rows of C per workgroup tile                                           */
@@ -138,8 +161,8 @@ typedef struct {
                       * matrix instructions while the other reads its next operands (2 stages) */
 } fp8bs_config;
 
-/* The configuration fp8bs_gemm (route FP8BS_ROUTE_BS) or fp8mx_gemm (FP8BS_ROUTE_MX) uses for
- * this shape. Host-only and pure; returns FP8BS_E_SHAPE for shapes the route rejects. */
+/* The configuration fp8bs_gemm (route FP8BS_ROUTE_BS), fp8mx_gemm (FP8BS_ROUTE_MX) or
+ * fp8pt_gemm (FP8BS_ROUTE_PT) uses for this shape. Host-only and pure; returns FP8BS_E_SHAPE for shapes the route rejects. */
 int fp8bs_select_config(int route, int M, int N, int K, fp8bs_config *out);
 
 /* fp8bs_gemm / fp8mx_gemm with an explicit configuration. The (block_m, block_n, waves_m,
@@ -152,6 +175,8 @@ int fp8bs_gemm_with_config(const void *A, const float *a_scale, const void *B_pr
 int fp8mx_gemm_with_config(const void *A, const void *a_scale_packed, const void *B_prep,
                            const void *b_scale_packed, void *C, int M, int N, int K,
                            const fp8bs_config *config, hipStream_t stream);
+int fp8pt_gemm_with_config(const void *A, const float *a_scale, const void *B_prep, const float *b_scale,
+                           void *C, int M, int N, int K, const fp8bs_config *config, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * Diagnostic (not part of the GEMM): the matrix core's sustained fp8 rate on the caller's own

@@ -48,6 +48,21 @@ def run_mx(fb, y):
     return bits(C)
 
 
+def run_pt(fb, z, config=None):
+    """Route PT on workload.PTInputs-like z (a_scale [M], b_scale [N]); returns bf16 bits."""
+    A = to_dev(z.A)
+    sa = to_dev(np.ascontiguousarray(z.a_scale, dtype=np.float32))
+    sb = to_dev(np.ascontiguousarray(z.b_scale, dtype=np.float32))
+    Bp = fb.prep_weights(to_dev(z.B))
+    C = torch.empty((z.A.shape[0], z.B.shape[0]), dtype=torch.bfloat16, device=dev())
+    if config is None:
+        fb.fp8pt_gemm(A, sa, Bp, sb, C)
+    else:
+        fb.fp8pt_gemm_with_config(A, sa, Bp, sb, C, config)
+    torch.cuda.synchronize()
+    return bits(C)
+
+
 def parity(gpu_bits: np.ndarray, ref_bits: np.ndarray, name: str = "") -> dict:
     g = oracle_pkg.bf16_bits_to_f64(gpu_bits)
     r = oracle_pkg.bf16_bits_to_f64(ref_bits)

@@ -14,6 +14,10 @@ Gemm", Procedure step 1: fp32 dequantise, matmul, round to bf16; page "aiter PR 
     PT:  C[m,n] = bf16( a_s[m] * b_s[n] * sum_k A[m,k] B[n,k] )   (the promote-free twin,
          page "Flydsl Fp8 Blockscale Gemm", Bottleneck diagnosis item 2)
 
+and the activation quantisers that produce the GEMM's inputs (per 1x128 group fp32 scale
+amax/448 for route BS; per 1x32 group ue8m0 exponent for route MX; e4m3 codes nearest, ties
+to even, saturating at 448).
+
 with block sums exact in fp64 and one round-to-nearest-even from fp64 to bf16.
 
 Pins (tests/test_oracle_*.py): e4m3 decode against torch's float8_e4m3fn; ue8m0 decode
@@ -65,6 +69,12 @@ class Oracle:
                            ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_e4m3_decode.restype = ctypes.c_double
         lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        for name in ("oracle_quantize_bs", "oracle_quantize_mx"):
+            fn = getattr(lib, name)
+            fn.restype = None
+            fn.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
         lib.oracle_e8m0_decode.restype = ctypes.c_double
         lib.oracle_e8m0_decode.argtypes = [ctypes.c_uint8]
         lib.oracle_bf16_round.restype = ctypes.c_uint16
@@ -112,6 +122,33 @@ class Oracle:
            rows.ctypes.data_as(_c_int_p), rows.size, cols.ctypes.data_as(_c_int_p), cols.size,
            acc.ctypes.data, bits.ctypes.data)
         return acc, bits
+
+    def e4m3_encode(self, x: float) -> int:
+        return int(self.lib.oracle_e4m3_encode(float(x)))
+
+    def quantize_bs(self, x):
+        """Activation quantiser, route BS: x [M,K] fp32 -> (codes uint8 [M,K], scales fp32
+        [M,K/128], logical a_s[m,kb])."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        M, K = x.shape
+        if K % 128:
+            raise ValueError("K must be a multiple of 128")
+        codes = np.empty((M, K), np.uint8)
+        scale = np.empty((M, K // 128), np.float32)
+        self.lib.oracle_quantize_bs(x.ctypes.data, M, K, codes.ctypes.data, scale.ctypes.data)
+        return codes, scale
+
+    def quantize_mx(self, x):
+        """Activation quantiser, route MX: x [M,K] fp32 -> (codes uint8 [M,K], ue8m0 bytes
+        uint8 [M,K/32])."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        M, K = x.shape
+        if K % 32:
+            raise ValueError("K must be a multiple of 32")
+        codes = np.empty((M, K), np.uint8)
+        e8 = np.empty((M, K // 32), np.uint8)
+        self.lib.oracle_quantize_mx(x.ctypes.data, M, K, codes.ctypes.data, e8.ctypes.data)
+        return codes, e8
 
     def bs_gemm(self, A, a_scale, B, b_scale, rows=None, cols=None):
         """Route BS. A [M,K] and B [N,K] uint8 e4m3 codes; a_scale [M,K/128] fp32 (logical

@@ -217,9 +217,94 @@ void oracle_pt_gemm(const uint8_t *A, const float *a_scale, const uint8_t *B,
     }
 }
 
+/* ---- activation quantisers (the step before the GEMM) ---------------------------------
+ * Route BS (page "Flydsl Fp8 Blockscale Gemm", Procedure step 6, and the 1x128 activation
+ * groups of Mechanism A): per 1x128 group of a row, scale = amax / 448 in fp32 (1 for an
+ * all-zero group), codes = e4m3(x / scale), the division in fp32.
+ * Route MX (page "aiter PR #6370", "Why it is faster"): per 1x32 group, the smallest integer
+ * e with amax <= 448 * 2^e (clamped to [-127, 127]; 0 for an all-zero group) is stored as the
+ * ue8m0 byte e + 127, codes = e4m3(x * 2^-e) (exact scaling).
+ * The e4m3 encoding is the nearest finite code, ties to the code with an even mantissa, and
+ * saturates at +-448 (plainest reading: the pages quantise with scale amax/448, so in-range
+ * values never exceed 448 by more than a rounding step). */
+
+/* Nearest finite e4m3 code to x (|x| handled by search over all 127 finite magnitudes). */
+static uint8_t e4m3_encode_nearest(float x)
+{
+    const double a = fabs((double)x);
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 0x7E; c++) {
+        const double d = fabs(e4m3_decode((uint8_t)c) - a);
+        /* strictly closer, or equally close and even (ties to even mantissa) */
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(signbit(x) ? (best | 0x80) : best);
+}
+
+/* x [M, K] fp32 row-major -> codes [M, K], scale [M, K/128] fp32 (row-major, a_s[m, kb]). */
+void oracle_quantize_bs(const float *x, int M, int K, uint8_t *codes, float *scale)
+{
+    const int KB = K / 128;
+#pragma omp parallel for schedule(static)
+    for (int m = 0; m < M; m++) {
+        for (int kb = 0; kb < KB; kb++) {
+            const float *g = x + (size_t)m * K + (size_t)kb * 128;
+            float amax = 0.0f;
+            for (int k = 0; k < 128; k++)
+                if (fabsf(g[k]) > amax)
+                    amax = fabsf(g[k]);
+            float s = amax / 448.0f;
+            if (amax == 0.0f)
+                s = 1.0f;
+            scale[(size_t)m * KB + kb] = s;
+            for (int k = 0; k < 128; k++) {
+                const float q = g[k] / s;
+                codes[(size_t)m * K + (size_t)kb * 128 + k] = e4m3_encode_nearest(q);
+            }
+        }
+    }
+}
+
+/* x [M, K] fp32 row-major -> codes [M, K], e8m0 [M, K/32] bytes (row-major). */
+void oracle_quantize_mx(const float *x, int M, int K, uint8_t *codes, uint8_t *e8m0)
+{
+    const int G = K / 32;
+#pragma omp parallel for schedule(static)
+    for (int m = 0; m < M; m++) {
+        for (int gi = 0; gi < G; gi++) {
+            const float *g = x + (size_t)m * K + (size_t)gi * 32;
+            double amax = 0.0;
+            for (int k = 0; k < 32; k++)
+                if (fabs((double)g[k]) > amax)
+                    amax = fabs((double)g[k]);
+            int e = 0;
+            if (amax > 0.0) {
+                /* the smallest e with amax <= 448 * 2^e, by direct search */
+                e = -140;
+                while (amax > ldexp(448.0, e))
+                    e++;
+                if (e < -127)
+                    e = -127;
+                if (e > 127)
+                    e = 127;
+            }
+            e8m0[(size_t)m * G + gi] = (uint8_t)(e + 127);
+            for (int k = 0; k < 32; k++) {
+                const float q = (float)ldexp((double)g[k], -e);
+                codes[(size_t)m * K + (size_t)gi * 32 + k] = e4m3_encode_nearest(q);
+            }
+        }
+    }
+}
+
 /* Exposed so the tests can pin the codecs on their own. */
 double oracle_e4m3_decode(uint8_t c) { return e4m3_decode(c); }
 double oracle_e8m0_decode(uint8_t b) { return e8m0_decode(b); }
+uint8_t oracle_e4m3_encode(float x) { return e4m3_encode_nearest(x); }
 uint16_t oracle_bf16_round(double x) { return bf16_round_from_f64(x); }
 
 /* Number of OpenMP threads a parallel region would use (0 when built without OpenMP). */

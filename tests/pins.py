@@ -522,6 +522,97 @@ def pin_pt_scale_linearity(o, seed=15):
                           acc[np.ix_([0, 1, 3, 4, 5], [c for c in range(N) if c != 7])])
 
 
+def _torch_e4m3(x):
+    """torch's fp32 -> float8_e4m3fn cast (round to nearest even) of values clipped to +-448."""
+    t = torch.from_numpy(np.clip(np.asarray(x, dtype=np.float32), -448.0, 448.0))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_e4m3_encode_vs_torch(o, seed=16):
+    """The oracle's e4m3 encoder agrees with torch's cast on random values over the whole
+    range, on every e4m3 value, on every midpoint between neighbours (ties) and just off them,
+    on the subnormal range and beyond 448 (saturation)."""
+    rng = np.random.default_rng(seed)
+    vals = torch_e4m3_values()
+    fin = np.sort(np.unique(np.abs(vals[np.isfinite(vals)])))
+    mids = (fin[1:] + fin[:-1]) / 2
+    xs = np.concatenate([
+        rng.uniform(-460, 460, 3000), rng.standard_normal(2000) * np.exp2(rng.integers(-12, 9, 2000)),
+        fin, -fin, mids, -mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
+        np.nextafter(mids.astype(np.float32), np.float32(1000)), [448.0, 449.0, 464.0, 1e6, -1e6, 0.0, -0.0],
+        rng.uniform(-2.0 ** -6, 2.0 ** -6, 1000)]).astype(np.float32)
+    got = np.array([o.e4m3_encode(v) for v in xs], dtype=np.uint8)
+    want = _torch_e4m3(xs)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, [(float(xs[i]), int(got[i]), int(want[i])) for i in bad[:5]]
+
+
+def _quant_input(rng, M, K):
+    """Gaussian rows plus rows that stress the quantiser: all zero, one large value, tiny
+    values, exact e4m3 values scaled by powers of two."""
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[1] = 0
+    x[2] = rng.standard_normal(K).astype(np.float32) * np.float32(2.0 ** -20)
+    x[3, 5] = 3.0e5
+    vals = torch_e4m3_values()
+    fin = vals[np.isfinite(vals)]
+    x[4] = (rng.choice(fin, K) * 2.0 ** 7).astype(np.float32)
+    x[5, :] = -1.0
+    return x
+
+
+def pin_quantize_bs_vs_recipe(o, seed=17):
+    """Route-BS activation quantiser equals the seeded input recipe (an independent numpy /
+    torch implementation of the same definition), bit for bit."""
+    rng = np.random.default_rng(seed)
+    x = _quant_input(rng, 40, 512)
+    codes, scale = o.quantize_bs(x)
+    c2, s2 = workload.quantize_groups_fp32(x, 1, 128)
+    assert np.array_equal(scale.view(np.uint32), s2.view(np.uint32))
+    assert np.array_equal(codes, c2)
+
+
+def pin_quantize_mx_vs_recipe(o, seed=18):
+    """Route-MX activation quantiser equals the seeded input recipe, bit for bit."""
+    rng = np.random.default_rng(seed)
+    x = _quant_input(rng, 40, 512)
+    codes, e8 = o.quantize_mx(x)
+    c2, e2 = workload.quantize_mx(x)
+    assert np.array_equal(e8, e2)
+    assert np.array_equal(codes, c2)
+
+
+def pin_quantize_closed_form(o, seed=19):
+    """A group holding exact e4m3 values times 2^k with largest magnitude 448 * 2^k has scale
+    exactly 2^k (route BS) and exponent k (route MX), and its codes are those values."""
+    rng = np.random.default_rng(seed)
+    vals = torch_e4m3_values()
+    fin_codes = np.array([c for c in range(256) if np.isfinite(vals[c])], dtype=np.uint8)
+    M, K = 6, 256
+    codes = rng.choice(fin_codes, size=(M, K)).astype(np.uint8)
+    codes[:, ::32] = 0x7E  # 448 in every 32-group
+    ks = np.array([-5, -1, 0, 2, 7, 12])
+    x = (vals[codes] * np.exp2(ks)[:, None]).astype(np.float32)
+    c, s = o.quantize_bs(x)
+    assert np.array_equal(s, np.repeat(np.exp2(ks)[:, None], K // 128, axis=1).astype(np.float32))
+    neg0 = (codes == 0x80)  # -0 and +0 both encode zero; compare values
+    assert np.array_equal(np.where(neg0, 0, c), np.where(neg0, 0, codes))
+    c, e8 = o.quantize_mx(x)
+    assert np.array_equal(e8.astype(int) - 127, np.repeat(ks[:, None], K // 32, axis=1))
+    assert np.array_equal(np.where(neg0, 0, c), np.where(neg0, 0, codes))
+
+
+def pin_quantize_mx_exponent_minimal(o, seed=20):
+    """Every MX exponent is the smallest that keeps the group within 448 * 2^e (or the clamp)."""
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((30, 256)) * np.exp2(rng.integers(-30, 30, size=(30, 1)))).astype(np.float32)
+    _, e8 = o.quantize_mx(x)
+    amax = np.abs(x.reshape(30, 8, 32)).max(axis=2).astype(np.float64)
+    e = e8.astype(np.int64) - 127
+    assert np.all(amax <= np.ldexp(448.0, e))
+    assert np.all((e == -127) | (amax > np.ldexp(448.0, e - 1)))
+
+
 ALL_PINS = [
     pin_e4m3_decode, pin_e8m0_decode, pin_bf16_round_fp32_exact, pin_bf16_round_exact,
     pin_bs_brute_force, pin_bs_tiny_config_exact, pin_mx_brute_force, pin_closed_form_ones,
@@ -529,4 +620,6 @@ ALL_PINS = [
     pin_invariant_scale_doubling, pin_invariant_permutations, pin_invariant_zero_block,
     pin_invariant_cross_route, pin_invariant_mx_unit_and_lossless, pin_pt_brute_force,
     pin_pt_inputs_exact, pin_pt_closed_form_integers, pin_pt_cross_route_bs, pin_pt_scale_linearity,
+    pin_e4m3_encode_vs_torch, pin_quantize_bs_vs_recipe, pin_quantize_mx_vs_recipe,
+    pin_quantize_closed_form, pin_quantize_mx_exponent_minimal,
 ]

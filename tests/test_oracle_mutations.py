@@ -27,6 +27,11 @@ MUTATIONS = {
     "mx_group_boundary": ("k < g * 32 + 32", "k < g * 32 + 31"),
     "pt_b_scale_by_row": ("(double)a_scale[m] * (double)b_scale[n]", "(double)a_scale[m] * (double)b_scale[m]"),
     "pt_b_scale_dropped": ("dot * ((double)a_scale[m] * (double)b_scale[n])", "dot * (double)a_scale[m]"),
+    "quant_scale_447": ("float s = amax / 448.0f;", "float s = amax / 447.0f;"),
+    "quant_ties_odd": ("(d == best_d && (c & 1) == 0)", "(d == best_d && (c & 1) == 1)"),
+    "quant_mx_exponent_loose": ("while (amax > ldexp(448.0, e))", "while (amax >= ldexp(448.0, e))"),
+    "quant_zero_group_scale": ("            s = 1.0f;", "            s = 2.0f;"),
+    "quant_sign_lost": ("return (uint8_t)(signbit(x) ? (best | 0x80) : best);", "return (uint8_t)best;"),
     "pt_last_k_dropped": ("for (int k = 0; k < K; k++)\n                dot +=", "for (int k = 0; k < K - 1; k++)\n                dot +="),
 }
 

@@ -18,6 +18,10 @@ every input already resident in HBM. Prints ONE JSON line on stdout:
   ceiling_twin -- the promote-free twin (fp8pt_gemm: one scale per row of A and of B, applied
                   in the epilogue) on the route-BS shapes: the same matrix work without the
                   per-block promote; bs_over_twin is the promote's cost as a time ratio
+  quantiser    -- the activation quantisers (bf16 -> e4m3 codes + scales) on the activation
+                  shapes of narrow-N, K-light (route BS) and mxfp8 (route MX): time, GB/s of
+                  algorithmic traffic (2 B read + 1 B written per element, plus scales) and the
+                  fraction of the 8 TB/s HBM peak
   cpu_baseline -- the CPU oracle (fp64, OpenMP) on a bounded sample of output rows
   parity       -- sampled rows/columns of the timed output against the oracle
 
@@ -415,6 +419,40 @@ def main() -> int:
             del tc
             torch.cuda.empty_cache()
 
+        # the activation quantisers (bf16 activations -> e4m3 codes + the GEMM's scale layout):
+        # memory-bound, measured against HBM bandwidth on each route's activation shape
+        quant = {}
+        import fp8_block_scaled_e4m3_amd as fb
+        for qname, qroute in (("narrow_n", "bs"), ("k_light", "bs"), ("mxfp8", "mx")):
+            cfgq = workload.CONFIGS[qname]
+            Mq, Kq = cfgq["M"], cfgq["K"]
+            xq = torch.randn((Mq, Kq), dtype=torch.float32, device="cuda:0").to(torch.bfloat16)
+            Aq = torch.empty((Mq, Kq), dtype=torch.uint8, device="cuda:0")
+            if qroute == "bs":
+                Sq = torch.empty((Kq // 128, Mq), dtype=torch.float32, device="cuda:0")
+                qlaunch = lambda: fb.fp8bs_quantize_act(xq, Aq, Sq, stream)
+                qbytes = Mq * Kq * 3 + Mq * (Kq // 128) * 4
+            else:
+                Sq = torch.empty((Mq, Kq // 32), dtype=torch.uint8, device="cuda:0")
+                qlaunch = lambda: fb.fp8mx_quantize_act(xq, Aq, Sq, stream)
+                qbytes = Mq * Kq * 3 + Mq * (Kq // 32)
+            for _ in range(200):
+                qlaunch()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(200):
+                qlaunch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            qt = e0.elapsed_time(e1) / 1e3 / 200
+            quant[f"{qroute}_{Mq}x{Kq}_bf16"] = dict(us=round(qt * 1e6, 2), bytes=qbytes,
+                                                    gbs=round(qbytes / qt / 1e9, 1),
+                                                    frac_hbm=round(qbytes / qt / 1e9 / PEAK_HBM_GBS, 3))
+            log(f"[bench] quantiser {qroute} {Mq}x{Kq}: {quant[f'{qroute}_{Mq}x{Kq}_bf16']}")
+            del xq, Aq, Sq
+
     case = main_row["case"]
     value = case.flops / main_row["wall"] / 1e12
     achieved = case.flops / main_row["ev"] / 1e12
@@ -443,6 +481,7 @@ def main() -> int:
         "cpu_baseline": main_row["baseline"],
         "per_shape": per_shape,
         "ceiling_twin": twin,
+        "quantiser": quant,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "kernel_source_sha256": kernel_source_hash()[:16]},
     }

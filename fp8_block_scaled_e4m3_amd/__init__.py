@@ -28,6 +28,7 @@ __all__ = [
     "prep_weights", "mx_prep_weights", "mx_pack_a_scale",
     "Config", "ROUTE_BS", "ROUTE_MX", "fp8bs_select_config", "fp8bs_gemm_with_config", "fp8mx_gemm_with_config",
     "fp8bs_mfma_ceiling", "ROUTE_PT", "fp8pt_gemm", "fp8pt_gemm_with_config",
+    "IN_F32", "IN_BF16", "fp8bs_quantize_act", "fp8mx_quantize_act", "quantize_bs", "quantize_mx",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -50,10 +51,14 @@ SIGNATURES = {
     "fp8mx_gemm_with_config": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp, _vp]),
     "fp8bs_mfma_ceiling": (_int, [_vp, _vp, _int, _int, _int, _int, _vp, _int, _vp, _vp]),
     "fp8pt_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp]),
+    "fp8bs_quantize_act": (_int, [_vp, _int, _vp, _vp, _int, _int, _vp]),
+    "fp8mx_quantize_act": (_int, [_vp, _int, _vp, _vp, _int, _int, _vp]),
     "fp8pt_gemm_with_config": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp, _vp]),
 }
 
 ROUTE_BS, ROUTE_MX, ROUTE_PT = 0, 1, 2
+IN_F32, IN_BF16 = 0, 1
+_IN_DTYPE = {torch.float32: IN_F32, torch.bfloat16: IN_BF16}
 
 
 class Config(ctypes.Structure):
@@ -190,6 +195,20 @@ def fp8pt_gemm_with_config(A, a_scale, B_prep, b_scale, C, config: Config, strea
     return C
 
 
+def fp8bs_quantize_act(x: torch.Tensor, A_codes: torch.Tensor, a_scale: torch.Tensor, stream=None) -> None:
+    """x [M,K] bf16/fp32 -> A_codes [M,K] uint8 e4m3, a_scale [K/128, M] fp32 (route BS)."""
+    M, K = x.shape
+    _check("fp8bs_quantize_act", lib.fp8bs_quantize_act(_ptr(x), _IN_DTYPE.get(x.dtype, -1), _ptr(A_codes),
+                                                        _ptr(a_scale), M, K, _stream(stream)))
+
+
+def fp8mx_quantize_act(x: torch.Tensor, A_codes: torch.Tensor, a_e8m0: torch.Tensor, stream=None) -> None:
+    """x [M,K] bf16/fp32 -> A_codes [M,K] uint8 e4m3, a_e8m0 [M, K/32] uint8 (route MX)."""
+    M, K = x.shape
+    _check("fp8mx_quantize_act", lib.fp8mx_quantize_act(_ptr(x), _IN_DTYPE.get(x.dtype, -1), _ptr(A_codes),
+                                                        _ptr(a_e8m0), M, K, _stream(stream)))
+
+
 def fp8bs_select_config(route: int, M: int, N: int, K: int) -> Config:
     cfg = Config()
     _check("fp8bs_select_config", lib.fp8bs_select_config(route, M, N, K, ctypes.byref(cfg)))
@@ -242,6 +261,24 @@ def mx_prep_weights(B: torch.Tensor, b_e8m0: torch.Tensor, stream=None):
     packed = torch.empty(fp8mx_packed_scale_bytes(N, K), dtype=torch.uint8, device=B.device)
     fp8mx_prep_weights(B, b_e8m0, B_prep, packed, stream)
     return B_prep, packed
+
+
+def quantize_bs(x: torch.Tensor, stream=None):
+    """(A codes [M,K] uint8, a_scale [K/128, M] fp32) for route BS from activations x."""
+    M, K = x.shape
+    A = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    sa = torch.empty((K // 128, M), dtype=torch.float32, device=x.device)
+    fp8bs_quantize_act(x, A, sa, stream)
+    return A, sa
+
+
+def quantize_mx(x: torch.Tensor, stream=None):
+    """(A codes [M,K] uint8, a_e8m0 [M, K/32] uint8) for route MX from activations x."""
+    M, K = x.shape
+    A = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    e8 = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    fp8mx_quantize_act(x, A, e8, stream)
+    return A, e8
 
 
 def mx_pack_a_scale(a_e8m0: torch.Tensor, stream=None) -> torch.Tensor:

@@ -325,6 +325,32 @@ int fp8pt_gemm_with_config(const void* A, const float* a_scale, const void* B_pr
     return run(fp8bs::kRoutePT, A, a_scale, B_prep, b_scale, C, M, N, K, config, stream);
 }
 
+static int quantize(int route, const void* x, int x_dtype, void* codes, void* scales, int M, int K, int group,
+                    size_t scale_align, hipStream_t stream)
+{
+    if (M < 0 || K < group || K % group != 0)
+        return FP8BS_E_SHAPE;
+    if (x_dtype != FP8BS_IN_F32 && x_dtype != FP8BS_IN_BF16)
+        return FP8BS_E_CONFIG;
+    if (M == 0)
+        return FP8BS_OK;
+    if (!x || !codes || !scales)
+        return FP8BS_E_NULL;
+    if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, scale_align))
+        return FP8BS_E_ALIGN;
+    return hip_status(fp8bs::launch_quantize(route, x, x_dtype == FP8BS_IN_BF16, codes, scales, M, K, stream));
+}
+
+int fp8bs_quantize_act(const void* x, int x_dtype, void* A_codes, float* a_scale, int M, int K, hipStream_t stream)
+{
+    return quantize(fp8bs::kRouteBS, x, x_dtype, A_codes, a_scale, M, K, 128, 4, stream);
+}
+
+int fp8mx_quantize_act(const void* x, int x_dtype, void* A_codes, void* a_e8m0, int M, int K, hipStream_t stream)
+{
+    return quantize(fp8bs::kRouteMX, x, x_dtype, A_codes, a_e8m0, M, K, 32, 1, stream);
+}
+
 int fp8bs_mfma_ceiling(const void* A, const void* B_prep, int M, int N, int K, int iters, float* sink, int sink_len,
                        long long* flops, hipStream_t stream)
 {

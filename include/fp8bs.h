@@ -77,6 +77,32 @@ size_t fp8bs_prep_weight_bytes(int N, int K);
 int fp8bs_prep_weights(const void *B, void *B_prep, int N, int K, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Activation quantisers (the step before the GEMM: page "Flydsl Fp8 Blockscale Gemm",
+ * Procedure step 6; page "aiter PR #6370", Integration). x is [M, K] row-major, bf16 or fp32.
+ * e4m3 codes are the nearest value, ties to the even mantissa, saturating at +-448; a NaN
+ * element encodes as NaN and is left out of its group's amax. Memory-bound, one pass.
+ * ------------------------------------------------------------------------------------------ */
+
+enum { FP8BS_IN_F32 = 0, FP8BS_IN_BF16 = 1 };
+
+/* Route BS activations: per 1x128 group of a row, scale = amax / 448 (fp32; 1 for an all-zero
+ * group), codes = e4m3(x / scale) with the division correctly rounded in fp32.
+ *   A_codes [M, K] e4m3 (the A operand of fp8bs_gemm); a_scale [K/128, M] fp32, K-block-major
+ *   (the a_scale operand of fp8bs_gemm).
+ * Constraints: M >= 0, K % 128 == 0, K >= 128; x and A_codes 16-byte aligned, a_scale 4-byte
+ * aligned; x_dtype is FP8BS_IN_F32 or FP8BS_IN_BF16 (else FP8BS_E_CONFIG). */
+int fp8bs_quantize_act(const void *x, int x_dtype, void *A_codes, float *a_scale, int M, int K,
+                       hipStream_t stream);
+
+/* Route MX activations: per 1x32 group, the smallest integer e with amax <= 448 * 2^e
+ * (clamped to [-127, 127]; 0 for an all-zero group), stored as the ue8m0 byte e + 127;
+ * codes = e4m3(x * 2^-e).
+ *   A_codes [M, K] e4m3; a_e8m0 [M, K/32] bytes, row-major (pack it with fp8mx_pack_a_scale).
+ * Constraints: M >= 0, K % 32 == 0, K >= 32; x and A_codes 16-byte aligned. */
+int fp8mx_quantize_act(const void *x, int x_dtype, void *A_codes, void *a_e8m0, int M, int K,
+                       hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * Route BS.
  * ------------------------------------------------------------------------------------------ */
 

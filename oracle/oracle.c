@@ -226,11 +226,14 @@ void oracle_pt_gemm(const uint8_t *A, const float *a_scale, const uint8_t *B,
  * ue8m0 byte e + 127, codes = e4m3(x * 2^-e) (exact scaling).
  * The e4m3 encoding is the nearest finite code, ties to the code with an even mantissa, and
  * saturates at +-448 (plainest reading: the pages quantise with scale amax/448, so in-range
- * values never exceed 448 by more than a rounding step). */
+ * values never exceed 448 by more than a rounding step). A NaN element encodes as NaN and is
+ * left out of its group's amax (the pages say nothing about NaN inputs). */
 
 /* Nearest finite e4m3 code to x (|x| handled by search over all 127 finite magnitudes). */
 static uint8_t e4m3_encode_nearest(float x)
 {
+    if (isnan(x))
+        return signbit(x) ? 0xFF : 0x7F;
     const double a = fabs((double)x);
     int best = 0;
     double best_d = INFINITY;
@@ -255,14 +258,14 @@ void oracle_quantize_bs(const float *x, int M, int K, uint8_t *codes, float *sca
             const float *g = x + (size_t)m * K + (size_t)kb * 128;
             float amax = 0.0f;
             for (int k = 0; k < 128; k++)
-                if (fabsf(g[k]) > amax)
+                if (fabsf(g[k]) > amax)  /* false for NaN: NaN is left out */
                     amax = fabsf(g[k]);
             float s = amax / 448.0f;
             if (amax == 0.0f)
                 s = 1.0f;
             scale[(size_t)m * KB + kb] = s;
             for (int k = 0; k < 128; k++) {
-                const float q = g[k] / s;
+                const float q = isnan(g[k]) ? g[k] : g[k] / s;  /* NaN keeps its own sign */
                 codes[(size_t)m * K + (size_t)kb * 128 + k] = e4m3_encode_nearest(q);
             }
         }
@@ -294,7 +297,7 @@ void oracle_quantize_mx(const float *x, int M, int K, uint8_t *codes, uint8_t *e
             }
             e8m0[(size_t)m * G + gi] = (uint8_t)(e + 127);
             for (int k = 0; k < 32; k++) {
-                const float q = (float)ldexp((double)g[k], -e);
+                const float q = isnan(g[k]) ? g[k] : (float)ldexp((double)g[k], -e);
                 codes[(size_t)m * K + (size_t)gi * 32 + k] = e4m3_encode_nearest(q);
             }
         }

@@ -541,6 +541,7 @@ def pin_e4m3_encode_vs_torch(o, seed=16):
         fin, -fin, mids, -mids, np.nextafter(mids.astype(np.float32), np.float32(0)),
         np.nextafter(mids.astype(np.float32), np.float32(1000)), [448.0, 449.0, 464.0, 1e6, -1e6, 0.0, -0.0],
         rng.uniform(-2.0 ** -6, 2.0 ** -6, 1000)]).astype(np.float32)
+    xs = np.concatenate([xs, np.array([np.nan, -np.nan], np.float32)])
     got = np.array([o.e4m3_encode(v) for v in xs], dtype=np.uint8)
     want = _torch_e4m3(xs)
     bad = np.flatnonzero(got != want)

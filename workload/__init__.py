@@ -16,8 +16,16 @@ synthetic values standing in for the model activations and weights measured ther
   smallest integer with ``amax <= 448 * 2^e`` (clamped to [-127, 127]; byte ``e + 127``;
   byte 127 when the group is all zero), and codes ``e4m3_rne_saturate(x * 2^-e)``.
 
+* Route PT (the promote-free twin): A and B are quantised per whole row with the fp32 scale
+  ``s = amax / 448`` of the row.
+
 The e4m3 encoder is torch's fp32 -> float8_e4m3fn conversion (round to nearest even) applied
 after clamping to +-448.
+
+Workloads (``CONFIGS``): the four shapes of that table (narrow-N 4096x2048x7168, K-light
+16384x7168x768, wide-N 4096x65536x1536 and the page's untuned narrow-N deep-K shape
+16384x1536x7168) plus the tiny 128x256x512 case (route BS), and the mxfp8 16384x8192x1280
+case of page "aiter PR #6370" (route MX).
 """
 from __future__ import annotations
 
@@ -35,6 +43,8 @@ CONFIGS = {
     "k_light": dict(M=16384, N=7168, K=768, route="bs"),
     "wide_n": dict(M=4096, N=65536, K=1536, route="bs"),
     "mxfp8": dict(M=16384, N=8192, K=1280, route="mx"),
+    # a second narrow-N, deep-K shape of the same class as narrow_n, untuned on the pages
+    "narrow_n_16k": dict(M=16384, N=1536, K=7168, route="bs"),
 }
 
 

@@ -22,6 +22,9 @@ every input already resident in HBM. Prints ONE JSON line on stdout:
                   shapes of narrow-N, K-light (route BS) and mxfp8 (route MX): time, GB/s of
                   algorithmic traffic (2 B read + 1 B written per element, plus scales) and the
                   fraction of the 8 TB/s HBM peak
+  small_m      -- few activation rows (M = 1, 16, 64: the decode regime) against the weights of
+                  each workload: hot and cold time, algorithmic GB/s and fraction of the HBM
+                  peak of the cold launch, the small-M kernel beside the main kernel
   cpu_baseline -- the CPU oracle (fp64, OpenMP) on a bounded sample of output rows
   parity       -- sampled rows/columns of the timed output against the oracle
 
@@ -82,7 +85,7 @@ def algorithmic_bytes(route: str, M: int, N: int, K: int) -> int:
 class Case:
     """Device-resident operands of one workload plus a launch closure on a given stream."""
 
-    def __init__(self, name: str, seed: int, stream, twin: bool = False):
+    def __init__(self, name: str, seed: int, stream, twin: bool = False, rows: int | None = None):
         import torch
 
         import fp8_block_scaled_e4m3_amd as fb
@@ -90,7 +93,9 @@ class Case:
 
         cfg = workload.CONFIGS[name]
         self.name, self.route = name, ("pt" if twin else cfg["route"])
-        self.M, self.N, self.K = cfg["M"], cfg["N"], cfg["K"]
+        self.M, self.N, self.K = (rows if rows is not None else cfg["M"]), cfg["N"], cfg["K"]
+        # route MX with fewer than 64 rows: the small-M entry, with row-major activation scales
+        small_mx = self.route == "mx" and self.M % 64 != 0
         dev = torch.device("cuda:0")
         t0 = time.time()
         if self.route == "pt":
@@ -111,16 +116,20 @@ class Case:
             y = workload.mx_inputs(self.M, self.N, self.K, seed)
             self.host = y
             self.A = torch.from_numpy(y.A).to(dev)
-            self.sa = fb.mx_pack_a_scale(torch.from_numpy(y.a_e8m0).to(dev), stream)
+            self.sa = torch.from_numpy(y.a_e8m0).to(dev)
+            if not small_mx:
+                self.sa = fb.mx_pack_a_scale(self.sa, stream)
             self.B, self.sb = fb.mx_prep_weights(torch.from_numpy(y.B).to(dev),
                                                  torch.from_numpy(y.b_e8m0).to(dev), stream)
         self.C = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
         log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s")
-        fn = {"bs": fb.fp8bs_gemm, "mx": fb.fp8mx_gemm, "pt": fb.fp8pt_gemm}[self.route]
+        fn = {"bs": fb.fp8bs_gemm, "mx": fb.fp8mx_gemm_small_m if small_mx else fb.fp8mx_gemm,
+              "pt": fb.fp8pt_gemm}[self.route]
         self.launch = lambda: fn(self.A, self.sa, self.B, self.sb, self.C, stream)
         route_id = {"bs": fb.ROUTE_BS, "mx": fb.ROUTE_MX, "pt": fb.ROUTE_PT}[self.route]
-        self.config = fb.fp8bs_select_config(route_id, self.M, self.N, self.K).as_dict()
+        self.config = {"small_m": 1} if small_mx else \
+            fb.fp8bs_select_config(route_id, self.M, self.N, self.K).as_dict()
 
     @property
     def flops(self) -> int:
@@ -453,6 +462,35 @@ def main() -> int:
             log(f"[bench] quantiser {qroute} {Mq}x{Kq}: {quant[f'{qroute}_{Mq}x{Kq}_bf16']}")
             del xq, Aq, Sq
 
+        # few rows (the decode regime): the weights dominate the traffic, so the bound is HBM.
+        # Hot = back-to-back launches (weights may stay in the MALL between launches), cold =
+        # single launches after a 1 GiB write; the main kernel with a fixed tile beside it.
+        small = {}
+        for wname in ("narrow_n", "k_light", "narrow_n_16k", "wide_n", "mxfp8"):
+            for rows in (1, 16, 64):
+                dc = Case(wname, 0, stream, rows=rows)
+                _, ev, _ = dc.steady_state(stream, 0.03, 0.03)
+                cold_med, _ = dc.cold(stream, scratch, reps=9)
+                nb = algorithmic_bytes(dc.route, dc.M, dc.N, dc.K)
+                row = dict(M=dc.M, N=dc.N, K=dc.K, route=dc.route, small_m=dc.config.get("small_m", 0),
+                           us=round(ev * 1e6, 2), cold_us=round(cold_med * 1e6, 2), bytes=nb,
+                           cold_gbs=round(nb / cold_med / 1e9, 1),
+                           cold_frac_hbm=round(nb / cold_med / 1e9 / PEAK_HBM_GBS, 3))
+                if dc.route == "bs":
+                    main_cfg = fb.Config(256, 128, 4, 2, 3, 4, 1, 1, 0) if dc.N // 128 >= 256 else \
+                        fb.Config(128, 128, 2, 2, 3, 4, 1, 1, 0)
+                    dc.launch = lambda dc=dc, c=main_cfg: fb.fp8bs_gemm_with_config(
+                        dc.A, dc.sa, dc.B, dc.sb, dc.C, c, stream)
+                    _, evm, _ = dc.steady_state(stream, 0.03, 0.03)
+                    cold_m, _ = dc.cold(stream, scratch, reps=9)
+                    row.update(main_kernel_us=round(evm * 1e6, 2), main_kernel_cold_us=round(cold_m * 1e6, 2),
+                               main_kernel_tile=f"{main_cfg.block_m}x{main_cfg.block_n}")
+                small[f"{wname}_weights_M{rows}"] = row
+                log(f"[bench] small-M {wname} M={rows}: {row}")
+                dc.free()
+                del dc
+            torch.cuda.empty_cache()
+
     case = main_row["case"]
     value = case.flops / main_row["wall"] / 1e12
     achieved = case.flops / main_row["ev"] / 1e12
@@ -482,6 +520,7 @@ def main() -> int:
         "per_shape": per_shape,
         "ceiling_twin": twin,
         "quantiser": quant,
+        "small_m": small,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "kernel_source_sha256": kernel_source_hash()[:16]},
     }

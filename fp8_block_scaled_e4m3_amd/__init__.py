@@ -29,6 +29,7 @@ __all__ = [
     "Config", "ROUTE_BS", "ROUTE_MX", "fp8bs_select_config", "fp8bs_gemm_with_config", "fp8mx_gemm_with_config",
     "fp8bs_mfma_ceiling", "ROUTE_PT", "fp8pt_gemm", "fp8pt_gemm_with_config",
     "IN_F32", "IN_BF16", "fp8bs_quantize_act", "fp8mx_quantize_act", "quantize_bs", "quantize_mx",
+    "fp8mx_gemm_small_m",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -52,6 +53,7 @@ SIGNATURES = {
     "fp8bs_mfma_ceiling": (_int, [_vp, _vp, _int, _int, _int, _int, _vp, _int, _vp, _vp]),
     "fp8pt_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp]),
     "fp8bs_quantize_act": (_int, [_vp, _int, _vp, _vp, _int, _int, _vp]),
+    "fp8mx_gemm_small_m": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp]),
     "fp8mx_quantize_act": (_int, [_vp, _int, _vp, _vp, _int, _int, _vp]),
     "fp8pt_gemm_with_config": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp, _vp]),
 }
@@ -65,7 +67,7 @@ class Config(ctypes.Structure):
     """fp8bs_config of include/fp8bs.h."""
     _fields_ = [(n, ctypes.c_int) for n in
                 ("block_m", "block_n", "waves_m", "waves_n", "stages", "group_m", "xcd_remap", "persistent",
-                 "pingpong")]
+                 "pingpong", "small_m")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}
@@ -207,6 +209,16 @@ def fp8mx_quantize_act(x: torch.Tensor, A_codes: torch.Tensor, a_e8m0: torch.Ten
     M, K = x.shape
     _check("fp8mx_quantize_act", lib.fp8mx_quantize_act(_ptr(x), _IN_DTYPE.get(x.dtype, -1), _ptr(A_codes),
                                                         _ptr(a_e8m0), M, K, _stream(stream)))
+
+
+def fp8mx_gemm_small_m(A: torch.Tensor, a_e8m0: torch.Tensor, B_prep: torch.Tensor, b_scale_packed: torch.Tensor,
+                       C: torch.Tensor, stream=None) -> torch.Tensor:
+    """Route MX for M <= 64: a_e8m0 [M, K/32] uint8 row-major (not packed)."""
+    M, K = A.shape
+    N = C.shape[1]
+    _check("fp8mx_gemm_small_m", lib.fp8mx_gemm_small_m(_ptr(A), _ptr(a_e8m0), _ptr(B_prep), _ptr(b_scale_packed),
+                                                        _ptr(C), M, N, K, _stream(stream)))
+    return C
 
 
 def fp8bs_select_config(route: int, M: int, N: int, K: int) -> Config:

@@ -4,6 +4,8 @@
 #include "fp8bs.h"
 #include "launch.hpp"
 
+#include <cstring>
+
 #include <stdint.h>
 
 namespace {
@@ -71,6 +73,16 @@ fp8bs_config make_config(int variant, int group_m, int xcd_remap, int persistent
     c.group_m = group_m;
     c.xcd_remap = xcd_remap;
     c.persistent = persistent;
+    c.small_m = 0;
+    return c;
+}
+
+// The small-M kernel: the tile fields do not apply to it and are zeroed.
+fp8bs_config small_m_config()
+{
+    fp8bs_config c;
+    memset(&c, 0, sizeof(c));
+    c.small_m = 1;
     return c;
 }
 
@@ -95,6 +107,16 @@ fp8bs_config select(int route, int M, int N, int K)
         const int xcd = group_m * (N / block_n) <= 2 * kCUs ? 1 : 2;
         return make_config(variant, group_m, xcd, 1);
     };
+    // Small M (the decode regime): the small-M kernel streams the weights once at close to
+    // HBM bandwidth; it wins for M <= 16 and, up to 64 rows, whenever the main kernel's tiles
+    // would not fill the CUs (measured: 7168 x 7168 weights, M = 1: 10.2 vs 37.6 us; with
+    // 65536 x 1536 weights the main kernel is faster from M = 32). Route MX reads its packed
+    // activation scales only in the main kernel (fp8mx_gemm_small_m is its small-M entry).
+    if (route != fp8bs::kRouteMX && M >= 1 && M <= fp8bs::kDecodeMaxRows) {
+        const int bm = 256, bn = N % 128 == 0 ? 128 : 64;
+        if (M <= 16 || ((M + bm - 1) / bm) * (N / bn) < kCUs)
+            return small_m_config();
+    }
     if ((route == fp8bs::kRouteMX || route == fp8bs::kRoutePT) && N % 128 != 0)
         return cfg(7, 64);
     if (N % 256 == 0 && tiles(256, 256) >= 2 * kCUs)
@@ -110,6 +132,8 @@ int check_config(int route, const fp8bs_config* c, int N, fp8bs::GemmConfig* out
 {
     if (!c)
         return FP8BS_E_NULL;
+    if (c->small_m != 0)
+        return FP8BS_E_CONFIG;  // handled by run()
     const int v = find_variant(*c);
     if (v < 0 || !fp8bs::variant_supports(route, v) || c->group_m < 1 || N % c->block_n != 0 ||
         (c->xcd_remap < 0 || c->xcd_remap > 2) || (c->persistent != 0 && c->persistent != 1))
@@ -124,11 +148,18 @@ int check_config(int route, const fp8bs_config* c, int N, fp8bs::GemmConfig* out
 int run(int route, const void* A, const void* a_scale, const void* B_prep, const void* b_scale, void* C,
         int M, int N, int K, const fp8bs_config* cfg, hipStream_t stream)
 {
+    fp8bs::GemmArgs args{A, a_scale, B_prep, b_scale, C, M, N, K, stream};
+    if (cfg && cfg->small_m == 1) {
+        // the small-M kernel reads the activation scales of route MX row-major, so the packed
+        // route-MX entry points cannot use it (fp8mx_gemm_small_m does)
+        if (route == fp8bs::kRouteMX || M > fp8bs::kDecodeMaxRows)
+            return FP8BS_E_CONFIG;
+        return hip_status(fp8bs::launch_decode(route, args));
+    }
     fp8bs::GemmConfig gc;
     int st = check_config(route, cfg, N, &gc);
     if (st != FP8BS_OK)
         return st;
-    fp8bs::GemmArgs args{A, a_scale, B_prep, b_scale, C, M, N, K, stream};
     return hip_status(fp8bs::launch_gemm(route, args, gc));
 }
 
@@ -349,6 +380,22 @@ int fp8bs_quantize_act(const void* x, int x_dtype, void* A_codes, float* a_scale
 int fp8mx_quantize_act(const void* x, int x_dtype, void* A_codes, void* a_e8m0, int M, int K, hipStream_t stream)
 {
     return quantize(fp8bs::kRouteMX, x, x_dtype, A_codes, a_e8m0, M, K, 32, 1, stream);
+}
+
+int fp8mx_gemm_small_m(const void* A, const void* a_e8m0, const void* B_prep, const void* b_scale_packed, void* C,
+                       int M, int N, int K, hipStream_t stream)
+{
+    if (M < 0 || M > fp8bs::kDecodeMaxRows || N < 64 || N % 64 != 0 || K < 256 || K % 128 != 0 ||
+        !fits_offsets(M, N, K))
+        return FP8BS_E_SHAPE;
+    if (M == 0)
+        return FP8BS_OK;
+    if (!A || !a_e8m0 || !B_prep || !b_scale_packed || !C)
+        return FP8BS_E_NULL;
+    if (!aligned(A, 16) || !aligned(B_prep, 16) || !aligned(C, 16) || !aligned(b_scale_packed, 16))
+        return FP8BS_E_ALIGN;
+    fp8bs::GemmArgs args{A, a_e8m0, B_prep, b_scale_packed, C, M, N, K, stream};
+    return hip_status(fp8bs::launch_decode(fp8bs::kRouteMX, args));
 }
 
 int fp8bs_mfma_ceiling(const void* A, const void* B_prep, int M, int N, int K, int iters, float* sink, int sink_len,

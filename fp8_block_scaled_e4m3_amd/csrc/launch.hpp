@@ -38,6 +38,12 @@ hipError_t launch_mfma_ceiling(const void* A, const void* B_prep, int M, int N, 
                                int sink_len, long long* flops, hipStream_t stream);
 hipError_t launch_prep_weights(const void* B, void* B_prep, int N, int K, hipStream_t stream);
 hipError_t launch_pack_scales(const void* e8m0, void* packed, int rows, int K, int permute, hipStream_t stream);
+// Small-M kernel (decode.hip): M in [1, kDecodeMaxRows], N % 64 == 0, K % 128 == 0. Route BS
+// takes a_scale [K/128, M] fp32 as the main kernel does; route MX takes the activation
+// exponents row-major, a_e8m0 [M, K/32]; route PT a_scale [M], b_scale [N].
+constexpr int kDecodeMaxRows = 64;
+hipError_t launch_decode(int route, const GemmArgs& a);
+
 // Activation quantiser of route kRouteBS (scales: fp32 [K/128, M]) or kRouteMX (scales: ue8m0
 // bytes [M, K/32]); x is bf16 (in_bf16 = 1) or fp32 [M, K].
 hipError_t launch_quantize(int route, const void* x, int in_bf16, void* codes, void* scales, int M, int K,

@@ -162,6 +162,14 @@ int fp8mx_gemm(const void *A, const void *a_scale_packed, const void *B_prep,
 int fp8pt_gemm(const void *A, const float *a_scale, const void *B_prep, const float *b_scale,
                void *C, int M, int N, int K, hipStream_t stream);
 
+/* Route MX for M <= 64 rows (the decode regime): the small-M kernel, which streams the
+ * weights once. The activation exponents are taken row-major, a_e8m0 [M, K/32] bytes (biased
+ * by 127; the packed layout of fp8mx_pack_a_scale needs whole 64-row groups); B_prep and
+ * b_scale_packed come from fp8mx_prep_weights. Constraints: 0 <= M <= 64, N % 64 == 0,
+ * K % 128 == 0, K >= 256; A, B_prep, C and b_scale_packed 16-byte aligned. */
+int fp8mx_gemm_small_m(const void *A, const void *a_e8m0, const void *B_prep, const void *b_scale_packed,
+                       void *C, int M, int N, int K, hipStream_t stream);
+
 /* ------------------------------------------------------------------------------------------
  * Kernel configuration (introspection and ablation). The plain entry points pick a
  * configuration from (M, N, K) alone (page "Flydsl Fp8 Blockscale Gemm", Per-shape recipes:
@@ -185,6 +193,9 @@ typedef struct {
     int persistent;  /* 1: one workgroup per CU slot walks several tiles; 0: one per tile      */
     int pingpong;    /* 1: the two halves of an 8-wave workgroup alternate, one running its    *
                       * matrix instructions while the other reads its next operands (2 stages) */
+    int small_m;     /* 1: the small-M kernel (M <= 64; every other field is ignored): one      *
+                      * workgroup per 16 output columns streams the weights once, its 8 waves  *
+                      * split K (routes BS and PT; route MX through fp8mx_gemm_small_m)         */
 } fp8bs_config;
 
 /* The configuration fp8bs_gemm (route FP8BS_ROUTE_BS), fp8mx_gemm (FP8BS_ROUTE_MX) or

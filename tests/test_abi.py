@@ -96,7 +96,17 @@ def test_select_config_is_shape_driven(fb):
     for route, shape in ((fb.ROUTE_BS, (4096, 65536, 1536)), (fb.ROUTE_MX, (16384, 8192, 1280)),
                          (fb.ROUTE_BS, (128, 256, 512)), (fb.ROUTE_BS, (1, 128, 128))):
         c = fb.fp8bs_select_config(route, *shape)
-        assert shape[1] % c.block_n == 0 and c.group_m >= 1
+        assert c.small_m == 1 or (shape[1] % c.block_n == 0 and c.group_m >= 1)
+    # few rows (the decode regime): the small-M kernel for routes BS and PT when M <= 16, or up
+    # to 64 rows while the main kernel's 256x128 tiles would not fill the 256 CUs
+    for route, shape, small in ((fb.ROUTE_BS, (1, 128, 128), 1), (fb.ROUTE_BS, (16, 65536, 1536), 1),
+                                (fb.ROUTE_BS, (64, 2048, 7168), 1), (fb.ROUTE_BS, (64, 65536, 1536), 0),
+                                (fb.ROUTE_BS, (65, 128, 7168), 0), (fb.ROUTE_PT, (33, 4096, 512), 1),
+                                (fb.ROUTE_PT, (0, 4096, 512), 0), (fb.ROUTE_MX, (64, 4096, 512), 0)):
+        c = fb.fp8bs_select_config(route, *shape)
+        assert c.small_m == small, (route, shape)
+        if small:
+            assert (c.block_m, c.block_n, c.stages) == (0, 0, 0)
 
 
 def test_select_config_rejects_bad_input(fb):

@@ -1,0 +1,112 @@
+"""The small-M kernel (M <= 64, the decode regime) on the GPU through the C ABI: full-C parity
+with the oracle for routes BS, PT and MX over row counts that fill 1 to 4 sixteen-row blocks
+(ragged included) and K ranges that leave some of the 8 waves without K blocks; bit-exact on
+integer operands; the plain entry points pick it by shape; errors are rejected."""
+import numpy as np
+import pytest
+import torch
+
+import workload
+from gpu_util import bits, dev, parity, run_bs, run_pt, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fb():
+    import fp8_block_scaled_e4m3_amd as fb
+    return fb
+
+
+def _small(fb):
+    c = fb.Config()
+    c.small_m = 1
+    return c
+
+
+SHAPES = [(1, 128, 128), (5, 256, 256), (16, 384, 1024), (17, 512, 896), (33, 192, 2048), (64, 1024, 7168),
+          (40, 4096, 384)]
+
+
+def _run_bs_cfg(fb, x, cfg):
+    A, sa, sb = to_dev(x.A), to_dev(x.a_scale_kmajor), to_dev(x.b_scale)
+    C = torch.full((x.M, x.N), 3.0, dtype=torch.bfloat16, device=dev())
+    fb.fp8bs_gemm_with_config(A, sa, fb.prep_weights(to_dev(x.B)), sb, C, cfg)
+    torch.cuda.synchronize()
+    return bits(C)
+
+
+@pytest.mark.parametrize("M,N,K", [s for s in SHAPES if s[1] % 128 == 0])
+def test_small_m_bs(fb, oracle, M, N, K):
+    x = workload.bs_inputs(M, N, K, M + N)
+    got = _run_bs_cfg(fb, x, _small(fb))
+    _, ref = oracle.bs_gemm(x.A, x.a_scale, x.B, x.b_scale)
+    parity(got, ref, f"small-M bs {M}x{N}x{K}")
+    again = _run_bs_cfg(fb, x, _small(fb))
+    assert np.array_equal(got, again)  # deterministic: fixed-order sum of the 8 partials
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_small_m_pt(fb, oracle, M, N, K):
+    z = workload.pt_inputs(M, N, K, M * 7 + N)
+    got = run_pt(fb, z, _small(fb))
+    _, ref = oracle.pt_gemm(z.A, z.a_scale, z.B, z.b_scale)
+    parity(got, ref, f"small-M pt {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [s for s in SHAPES if s[2] >= 256])
+def test_small_m_mx(fb, oracle, M, N, K):
+    y = workload.mx_inputs(M, N, K, M + 3 * N)
+    Bp, pb = fb.mx_prep_weights(to_dev(y.B), to_dev(y.b_e8m0))
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
+    fb.fp8mx_gemm_small_m(to_dev(y.A), to_dev(y.a_e8m0), Bp, pb, C)
+    torch.cuda.synchronize()
+    _, ref = oracle.mx_gemm(y.A, y.a_e8m0, y.B, y.b_e8m0)
+    parity(bits(C), ref, f"small-M mx {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,K", [(7, 512), (48, 1280)])
+def test_small_m_integer_exact(fb, oracle, M, K):
+    """Small-integer codes with power-of-two scales: every partial and the fixed-order sum of
+    the wave partials are exact in fp32, so the output equals the oracle bit for bit."""
+    N = 256
+    rng = np.random.default_rng(M + K)
+    A = workload.e4m3_encode(rng.integers(-4, 5, size=(M, K)).astype(np.float32))
+    B = workload.e4m3_encode(rng.integers(-4, 5, size=(N, K)).astype(np.float32))
+    sa = np.exp2(rng.integers(-3, 4, size=(M, K // 128))).astype(np.float32)
+    sb = np.exp2(rng.integers(-3, 4, size=(N // 128, K // 128))).astype(np.float32)
+    x = workload.BSInputs(M, N, K, A, sa, B, sb)
+    got = _run_bs_cfg(fb, x, _small(fb))
+    _, ref = oracle.bs_gemm(A, sa, B, sb)
+    assert np.array_equal(got, ref)
+
+
+def test_plain_entry_picks_small_m(fb, oracle):
+    """fp8bs_gemm and fp8pt_gemm use the small-M kernel for few rows and narrow outputs, the
+    main kernel when the main kernel's tiles fill the device."""
+    assert fb.fp8bs_select_config(fb.ROUTE_BS, 8, 7168, 7168).small_m == 1
+    assert fb.fp8bs_select_config(fb.ROUTE_BS, 64, 2048, 7168).small_m == 1
+    assert fb.fp8bs_select_config(fb.ROUTE_BS, 64, 65536, 1536).small_m == 0
+    assert fb.fp8bs_select_config(fb.ROUTE_BS, 65, 2048, 7168).small_m == 0
+    assert fb.fp8bs_select_config(fb.ROUTE_PT, 1, 4096, 512).small_m == 1
+    assert fb.fp8bs_select_config(fb.ROUTE_MX, 64, 4096, 512).small_m == 0
+    x = workload.bs_inputs(24, 2048, 1024, 2)
+    got = run_bs(fb, x)  # plain entry point
+    assert np.array_equal(got, _run_bs_cfg(fb, x, _small(fb)))
+
+
+def test_small_m_rejects(fb):
+    x = workload.bs_inputs(65, 256, 256, 0)
+    with pytest.raises(fb.Fp8bsError) as e:
+        _run_bs_cfg(fb, x, _small(fb))
+    assert e.value.status == 4
+    d = dev()
+    A = torch.zeros((65, 256), dtype=torch.uint8, device=d)
+    buf = torch.zeros(1 << 16, dtype=torch.uint8, device=d)
+    C = torch.full((65, 256), 3.0, dtype=torch.bfloat16, device=d)
+    assert fb.lib.fp8mx_gemm_small_m(A.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), C.data_ptr(),
+                                     65, 256, 256, None) == 2
+    assert fb.lib.fp8mx_gemm_small_m(A.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), C.data_ptr(),
+                                     16, 256, 128, None) == 2
+    torch.cuda.synchronize()
+    assert torch.all(C == 3.0)

@@ -1,6 +1,6 @@
 // decode.hip -- the small-M ("decode") regime: M <= 64 rows of activations against a weight
 // matrix streamed once from HBM (page "Flydsl Fp8 Blockscale Gemm", When to use: the decode
-// variants; page "aiter PR #6370", Follow-ups: a GEMV-style kernel for M <= 32).
+// variants; page "aiter PR #6370", Not included: a separate GEMV-style kernel for M <= 32).
 //
 // With so few rows the GEMM is bound by reading B (N*K bytes) and a 128-row output tile would
 // leave most of every matrix instruction idle, so the work is cut the other way: a workgroup

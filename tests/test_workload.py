@@ -65,3 +65,15 @@ def test_generator_is_seeded():
     assert np.array_equal(a.A, b.A) and np.array_equal(a.B, b.B)
     assert not np.array_equal(a.A, c.A)
     assert torch.equal(torch.from_numpy(a.a_scale), torch.from_numpy(b.a_scale))
+
+
+def test_tiled_inputs_repeat_with_odd_periods():
+    x = workload.tiled_bs_inputs(300, 1024, 256, seed=3, row_period=37, block_period=3)
+    ref = workload.bs_inputs(37, 384, 256, seed=3)
+    assert np.array_equal(x.A[:37], ref.A) and np.array_equal(x.A[37:74], ref.A)
+    assert np.array_equal(x.a_scale[259:296], ref.a_scale)
+    assert np.array_equal(x.B[:384], ref.B) and np.array_equal(x.B[768:], ref.B[:256])
+    assert np.array_equal(x.b_scale[6:], ref.b_scale[:2])
+    y = workload.tiled_mx_inputs(100, 64, 256, seed=4, row_period=33)
+    yr = workload.mx_inputs(33, 33, 256, seed=4)
+    assert np.array_equal(y.A[66:99], yr.A) and np.array_equal(y.b_e8m0[33:64], yr.b_e8m0[:31])

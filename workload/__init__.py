@@ -169,6 +169,44 @@ def pt_inputs(M: int, N: int, K: int, seed: int = 0) -> PTInputs:
     return PTInputs(A, np.ascontiguousarray(sa.reshape(M)), B, np.ascontiguousarray(sb.reshape(N)))
 
 
+def tiled_bs_inputs(M: int, N: int, K: int, seed: int = 0, row_period: int = 8191,
+                    block_period: int = 67) -> BSInputs:
+    """Route-BS operands at sizes whose fp32 draw would not fit in host memory (M * K or N * K
+    near 2^31): the rows of A repeat with period `row_period` and the 128-row weight blocks
+    with period `block_period`, each period drawn and quantised as in bs_inputs, with the scales
+    repeating along. Both periods are odd, so a read displaced by a power-of-two number of
+    bytes lands on different data."""
+    rows_a = min(M, row_period)
+    blocks_b = min(N // 128, block_period)
+    a, b = draw(rows_a, blocks_b * 128, K, seed)
+    qa, sa = quantize_groups_fp32(a, 1, 128)
+    qb, sb = quantize_groups_fp32(b, 128, 128)
+    del a, b
+    reps_a = -(-M // rows_a)
+    A = np.tile(qa, (reps_a, 1))[:M]
+    a_scale = np.tile(sa, (reps_a, 1))[:M]
+    reps_b = -(-(N // 128) // blocks_b)
+    B = np.tile(qb, (reps_b, 1))[:N]
+    b_scale = np.tile(sb, (reps_b, 1))[:N // 128]
+    return BSInputs(M, N, K, np.ascontiguousarray(A), np.ascontiguousarray(a_scale), np.ascontiguousarray(B),
+                    np.ascontiguousarray(b_scale))
+
+
+def tiled_mx_inputs(M: int, N: int, K: int, seed: int = 0, row_period: int = 8191) -> MXInputs:
+    """Route-MX operands with the rows of A and of B repeating with an odd period (see
+    tiled_bs_inputs)."""
+    rows_a, rows_b = min(M, row_period), min(N, row_period)
+    a, b = draw(rows_a, rows_b, K, seed)
+    qa, ea = quantize_mx(a)
+    qb, eb = quantize_mx(b)
+    del a, b
+    ra, rb = -(-M // rows_a), -(-N // rows_b)
+    return MXInputs(M, N, K, np.ascontiguousarray(np.tile(qa, (ra, 1))[:M]),
+                    np.ascontiguousarray(np.tile(ea, (ra, 1))[:M]),
+                    np.ascontiguousarray(np.tile(qb, (rb, 1))[:N]),
+                    np.ascontiguousarray(np.tile(eb, (rb, 1))[:N]))
+
+
 def sample_indices(n_total: int, n_pick: int, seed: int) -> np.ndarray:
     """A seeded, sorted sample of distinct indices that always includes the first and last."""
     if n_pick >= n_total:

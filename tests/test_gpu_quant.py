@@ -2,7 +2,8 @@
 codes and scales bit for bit, for fp32 and bf16 input, on gaussian rows and rows that stress
 the encoder (all zero, one huge value, tiny values, exact e4m3 values times 2^k, NaN of
 either sign), at
-small, ragged and benchmark-sized shapes; then quantise -> GEMM end to end for both routes."""
+small, ragged and benchmark-sized shapes, and on every finite bf16 value under ~200 group
+maxima; then quantise -> GEMM end to end for both routes."""
 import numpy as np
 import pytest
 import torch
@@ -56,6 +57,59 @@ def test_quantize_bs_bitwise(fb, oracle, dtype, M, K):
     bad = np.flatnonzero(got != codes)
     assert bad.size == 0, [(int(i // K), int(i % K), float(xf.flat[i]), int(got.flat[i]), int(codes.flat[i]))
                            for i in bad[:5]]
+
+
+def _every_bf16_under(amaxes, group, K):
+    """Rows of bf16-exact fp32 values: for each amax, every finite bf16 value v with |v| <= amax,
+    in groups of `group` whose first element is amax (so amax is the group's amax)."""
+    u = np.arange(1 << 16, dtype=np.uint32) << 16
+    allv = u.view(np.float32)
+    allv = allv[np.isfinite(allv)]
+    groups = []
+    for a in amaxes:
+        v = allv[np.abs(allv) <= a]
+        v = np.concatenate([v, np.zeros((-len(v)) % (group - 1), np.float32)])
+        g = v.reshape(-1, group - 1)
+        groups.append(np.concatenate([np.full((len(g), 1), a, np.float32), g], axis=1))
+    x = np.concatenate(groups).reshape(-1)
+    x = np.concatenate([x, np.zeros((-len(x)) % K, np.float32)])
+    return x.reshape(-1, K)
+
+
+def _bf16_amaxes():
+    out = []
+    for e in range(-133, 128, 4):
+        for m in (1.0, 1.5078125, 1.9921875):
+            a = np.float32(np.ldexp(m, e))
+            b = torch.tensor([float(a)], dtype=torch.float32).to(torch.bfloat16).to(torch.float32).item()
+            if 0 < b < 3.4e38:
+                out.append(np.float32(b))
+    return sorted(set(out + [np.float32(448.0), np.float32(1.0), np.float32(3.5)]))
+
+
+@pytest.mark.parametrize("route", ["bs", "mx"])
+def test_quantize_every_bf16_value(fb, oracle, route):
+    """Every finite bf16 value, quantised in groups whose amax runs over ~200 values from the
+    subnormal range to near the bf16 maximum: codes and scales bit for bit. This covers every
+    (value, scale) pair of the encoder's arithmetic that bf16 input can reach at these scales,
+    ties and near-ties of the e4m3 rounding included."""
+    group = 128 if route == "bs" else 32
+    x = _every_bf16_under(_bf16_amaxes(), group, 1024)
+    print(f"{route}: {x.size} values", flush=True)
+    xd = torch.from_numpy(x).to(torch.bfloat16).to(dev())
+    if route == "bs":
+        A, sc = fb.quantize_bs(xd)
+        torch.cuda.synchronize()
+        codes, ref = oracle.quantize_bs(x)
+        assert np.array_equal(sc.cpu().numpy().T.view(np.uint32), ref.view(np.uint32)), "scales differ"
+    else:
+        A, sc = fb.quantize_mx(xd)
+        torch.cuda.synchronize()
+        codes, ref = oracle.quantize_mx(x)
+        assert np.array_equal(sc.cpu().numpy(), ref), "exponents differ"
+    got = A.cpu().numpy()
+    bad = np.flatnonzero(got != codes)
+    assert bad.size == 0, [(float(x.flat[i]), int(got.flat[i]), int(codes.flat[i])) for i in bad[:5]]
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

@@ -88,8 +88,9 @@ fp8bs_config small_m_config()
 
 // Shape-driven choice of the workgroup tile (page "Flydsl Fp8 Blockscale Gemm", Per-shape
 // recipes: selection by (M, N, K) alone, never by layer). Prefer the 256x256 tile when it
-// still gives at least two workgroups per CU, else the 128x256 / 256x128 tiles when they fill
-// the 256 CUs, else 128x128 (or 128x64 for MX with N not a multiple of 128).
+// still gives at least two workgroups per CU, else the 256x128 / 128x256 tiles (warp-
+// specialised schedule) when they fill the 256 CUs, else 128x128 (or 128x64 for MX with N not
+// a multiple of 128).
 fp8bs_config select(int route, int M, int N, int K)
 {
     (void)K;
@@ -121,10 +122,13 @@ fp8bs_config select(int route, int M, int N, int K)
         return cfg(7, 64);
     if (N % 256 == 0 && tiles(256, 256) >= 2 * kCUs)
         return cfg(2, 256);
+    // the 256x128 / 128x256 tiles run warp-specialised (four loader waves beside the eight
+    // math waves): measured 5-7% faster than the same tiles with every wave loading on the
+    // 4096 x 2048 x 7168 and 16384 x 1536 x 7168 shapes
     if (tiles(256, 128) >= kCUs)
-        return cfg(6, 128);
+        return cfg(13, 128);
     if (N % 256 == 0 && tiles(128, 256) >= kCUs)
-        return cfg(5, 256);
+        return cfg(14, 256);
     return cfg(0, 128);
 }
 

@@ -30,6 +30,11 @@
 //  * One barrier per step, placed after the last matrix instruction of the step is issued:
 //    the wave then reads the first fragments of the next step while its last instructions
 //    and the promotes still run.
+//  * Schedules (config field `pingpong`): 0, every wave loads and computes; 1, ping-pong (the
+//    two halves of the workgroup alternate memory and matrix phases); 2, warp-specialised:
+//    WM x WN math waves that only read LDS and run matrix instructions, plus four loader waves
+//    (one per SIMD) that only issue the global -> LDS loads, so the load-issue stalls of the
+//    texture path never hold up a wave that has matrix work to issue.
 //  * Tiles are handed out so that the workgroups running at the same time on one XCD (each
 //    XCD has its own L2) work on neighbouring tiles (page "Flydsl Fp8 Blockscale Gemm",
 //    Mechanism B: XCD-aware rasterisation).
@@ -54,7 +59,11 @@ constexpr int kLdsCapacity = 160 * 1024;
 
 template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES, int PP>
 struct Tile {
-    static constexpr int kWaves = WM * WN;
+    // PP == 2 (warp-specialised): WM x WN math waves plus four loader waves (one per SIMD:
+    // waves w, w+4, w+8 share a SIMD)
+    static constexpr int kMathWaves = WM * WN;
+    static constexpr int kWaves = PP == 2 ? kMathWaves + 4 : kMathWaves;
+    static constexpr int kLoaders = PP == 2 ? 4 : kWaves;  // waves that issue the loads
     static constexpr int kThreads = kWaves * 64;
     static constexpr int TM = BM / WM;
     static constexpr int TN = BN / WN;
@@ -67,14 +76,14 @@ struct Tile {
     static constexpr int kSABytes = ROUTE == kRoutePT ? 0 : BM * 4;
     static constexpr int kSBBytes = ROUTE == kRoutePT ? 0 : ROUTE == kRouteBS ? 256 : BN * 4;
     static constexpr int kStageBytes = kABytes + kBBytes + kSABytes + kSBBytes;
-    static constexpr int kLoadsA = BM / 8 / kWaves;  // 1 KB (8-row) loads per wave per step
-    static constexpr int kLoadsB = BN / 8 / kWaves;
+    static constexpr int kLoadsA = BM / 8 / kLoaders;  // 1 KB (8-row) loads per loading wave per step
+    static constexpr int kLoadsB = BN / 8 / kLoaders;
     static constexpr int kScaleLoadsA = ROUTE == kRoutePT ? 0 : BM / 64;  // 256-byte loads
     static constexpr int kScaleLoadsB = ROUTE == kRoutePT ? 0 : ROUTE == kRouteBS ? 1 : BN / 64;
     static constexpr int kScaleLoads = kScaleLoadsA + kScaleLoadsB;
-    static constexpr int kLoadsS = (kScaleLoads + kWaves - 1) / kWaves;
+    static constexpr int kLoadsS = (kScaleLoads + kLoaders - 1) / kLoaders;
     static constexpr int kLoadsPerStep = kLoadsA + kLoadsB + kLoadsS;
-    static_assert(BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "whole 8-row groups per wave");
+    static_assert(BM % (8 * kLoaders) == 0 && BN % (8 * kLoaders) == 0, "whole 8-row groups per wave");
     static_assert(BM % 64 == 0 && TM % 16 == 0 && TN % 64 == 0, "16x16 sub-tiles, 64-row scale loads, "
                   "whole 64-column windows of the prepared weight order per wave");
     static_assert(ROUTE == kRouteMX   ? (TM % 64 == 0 && TN % 64 == 0)
@@ -84,7 +93,8 @@ struct Tile {
     static_assert(STAGES >= 2 && STAGES <= 4, "2 to 4 LDS stages");
     static_assert(STAGES * kStageBytes <= kLdsCapacity, "LDS capacity");
     static_assert(kLoadsPerStep * (STAGES - 1) <= 63, "vmcnt range");
-    static_assert(PP == 0 || (STAGES == 2 && kWaves == 8), "ping-pong: two stages, two groups of four waves");
+    static_assert(PP != 1 || (STAGES == 2 && kWaves == 8), "ping-pong: two stages, two groups of four waves");
+    static_assert(PP != 2 || kMathWaves == 4 || kMathWaves == 8, "warp-specialised: 4 or 8 math waves");
 };
 
 // s_waitcnt for vmcnt <= N and lgkmcnt == 0 (expcnt left unconstrained).
@@ -174,7 +184,7 @@ __device__ __forceinline__ void tile_of(int u, int grid, int tiles_m, int tiles_
 }
 
 template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES, int PP>
-__global__ void __launch_bounds__(WM * WN * 64)
+__global__ void __launch_bounds__((WM * WN + (PP == 2 ? 4 : 0)) * 64)
 gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
             const uint8_t* __restrict__ B, const void* __restrict__ b_scale,
             uint16_t* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
@@ -193,6 +203,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM;
     const int wn = wave / WM;
+    const int lw = PP == 2 ? wave - T::kMathWaves : wave;  // index among the loading waves
     const int KB = K >> 7;
     const int T_total = tiles_m * tiles_n;
     const int grid = gridDim.x;
@@ -219,18 +230,18 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
         const int m0 = tm * BM, n0 = tn * BN;
 #pragma unroll
         for (int g = 0; g < T::kLoadsA; ++g) {
-            const int row = (wave * T::kLoadsA + g) * 8 + (lane >> 3);
+            const int row = (lw * T::kLoadsA + g) * 8 + (lane >> 3);
             const int m = min(m0 + row, M - 1);
             voffA[g] = (uint32_t)m * (uint32_t)K + ((((uint32_t)lane & 7u) ^ swz(row)) << 4);
         }
 #pragma unroll
         for (int g = 0; g < T::kLoadsB; ++g) {
-            const int row = (wave * T::kLoadsB + g) * 8 + (lane >> 3);
+            const int row = (lw * T::kLoadsB + g) * 8 + (lane >> 3);
             voffB[g] = (uint32_t)(n0 + row) * (uint32_t)K + ((((uint32_t)lane & 7u) ^ swz(row)) << 4);
         }
 #pragma unroll
         for (int g = 0; g < T::kLoadsS; ++g) {
-            const int u = min(wave * T::kLoadsS + g, T::kScaleLoads - 1);
+            const int u = min(lw * T::kLoadsS + g, T::kScaleLoads - 1);
             if (u < T::kScaleLoadsA) {
                 if constexpr (ROUTE == kRouteBS) {  // a_scale[kb*M + m], fp32
                     voffS[g] = (uint32_t)min(m0 + 64 * u + lane, M - 1) * 4u;
@@ -276,14 +287,14 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
         constexpr int g = decltype(G)::value;
         const int koff = __builtin_amdgcn_readfirstlane(ld_kbv * 128);
         if constexpr (g < T::kLoadsA) {
-            lds_dma<16>(rsA, lds_addr(st + (wave * T::kLoadsA + g) * 1024), (int)voffA[g], koff);
+            lds_dma<16>(rsA, lds_addr(st + (lw * T::kLoadsA + g) * 1024), (int)voffA[g], koff);
         } else if constexpr (g < T::kLoadsA + T::kLoadsB) {
             constexpr int gb = g - T::kLoadsA;
-            lds_dma<16>(rsB, lds_addr(st + T::kABytes + (wave * T::kLoadsB + gb) * 1024), (int)voffB[gb], koff);
+            lds_dma<16>(rsB, lds_addr(st + T::kABytes + (lw * T::kLoadsB + gb) * 1024), (int)voffB[gb], koff);
         } else {
             constexpr int gs = g - T::kLoadsA - T::kLoadsB;
             lds_u8* sS = st + T::kABytes + T::kBBytes;
-            const int u = min(wave * T::kLoadsS + gs, T::kScaleLoads - 1);  // uniform
+            const int u = min(lw * T::kLoadsS + gs, T::kScaleLoads - 1);  // uniform
             const int soff = __builtin_amdgcn_readfirstlane(ld_kbv * (int)kstrS[gs]);
             const bool is_a = u < T::kScaleLoadsA;
             const v4i rs = is_a ? rsSA : rsSB;
@@ -380,7 +391,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
         }
     };
 
-    if constexpr (PP) {
+    if constexpr (PP == 1) {
     // ---- ping-pong schedule ------------------------------------------------------------------
     // Waves w and w+4 share a SIMD, so the two groups (waves 0-3 and 4-7) each hold one wave of
     // every SIMD. Each group alternates a memory phase (read all of the step's fragments and
@@ -649,12 +660,12 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
                 // the next load group goes out spread over the step (kLoadSpacing instructions
                 // apart): a burst of loads fills the memory path's in-flight capacity and
                 // stalls the issuing wave, matrix instructions and all
-                if constexpr (t % kLoadSpacing == 0 && t / kLoadSpacing < T::kLoadsPerStep)
+                if constexpr (PP == 0 && t % kLoadSpacing == 0 && t / kLoadSpacing < T::kLoadsPerStep)
                     issue_load(std::integral_constant<int, t / kLoadSpacing>{}, load_st);
                 __builtin_amdgcn_sched_barrier(0);
             });
         });
-        if constexpr (T::kLoadsPerStep > NO * NH) {
+        if constexpr (PP == 0 && T::kLoadsPerStep > NO * NH) {
             static_for<T::kLoadsPerStep - NO * NH>(
                 [&](auto G) { issue_load(std::integral_constant<int, NO * NH + decltype(G)::value>{}, load_st); });
         }
@@ -719,6 +730,78 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
             ++cp_tile;
         }
     };
+    if constexpr (PP == 2) {
+        // Warp-specialised: waves kMathWaves.. only move data, the others only compute. Every
+        // wave passes one barrier before the first step and one per step.
+        if (wave >= T::kMathWaves) {
+            if (total > 0) {
+                static_for<STAGES - 1>([&](auto S) {
+                    plan_loads(decltype(S)::value < total);
+                    issue_group((lds_u8*)stage_ptr(S));
+                });
+                wait_vmcnt_lgkm<(STAGES - 2) * T::kLoadsPerStep>();
+                __builtin_amdgcn_s_barrier();
+            }
+            // in step s: the loads of step s + STAGES - 1 into the stage step s - 1 used, then
+            // wait until those of step s + 1 have landed
+            auto lstep = [&](auto S, int s) {
+                constexpr int kS = decltype(S)::value;
+                plan_loads(s + STAGES - 1 < total);
+                issue_group((lds_u8*)stage_ptr(std::integral_constant<int, (kS + STAGES - 1) % STAGES>{}));
+                wait_vmcnt_lgkm<(STAGES - 2) * T::kLoadsPerStep>();
+                __builtin_amdgcn_s_barrier();
+            };
+            for (int s = 0; s < total; s += STAGES) {
+                lstep(std::integral_constant<int, 0>{}, s);
+                if (s + 1 < total)
+                    lstep(std::integral_constant<int, 1>{}, s + 1);
+                if constexpr (STAGES > 2) {
+                    if (s + 2 < total)
+                        lstep(std::integral_constant<int, 2>{}, s + 2);
+                }
+                if constexpr (STAGES > 3) {
+                    if (s + 3 < total)
+                        lstep(std::integral_constant<int, 3>{}, s + 3);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            return;
+        }
+        auto mstep = [&](auto S, int s) {
+            constexpr int kS = decltype(S)::value;
+            uint8_t* cur = stage_ptr(S);
+            uint8_t* nxt = stage_ptr(std::integral_constant<int, (kS + 1) % STAGES>{});
+            rows(cur, (lds_u8*)nullptr, [&]() {
+                wait_lgkm0();  // this wave's reads of the stage are done
+                __builtin_amdgcn_s_barrier();
+                read_head(nxt);
+            });
+            if (++cp_kb == KB) {
+                store_tile(cp_tile);
+                cp_kb = 0;
+                ++cp_tile;
+            }
+        };
+        if (total > 0) {
+            __builtin_amdgcn_s_barrier();
+            read_head(st0);
+        }
+        for (int s = 0; s < total; s += STAGES) {
+            mstep(std::integral_constant<int, 0>{}, s);
+            if (s + 1 < total)
+                mstep(std::integral_constant<int, 1>{}, s + 1);
+            if constexpr (STAGES > 2) {
+                if (s + 2 < total)
+                    mstep(std::integral_constant<int, 2>{}, s + 2);
+            }
+            if constexpr (STAGES > 3) {
+                if (s + 3 < total)
+                    mstep(std::integral_constant<int, 3>{}, s + 3);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+    }
     if (total > 0) {
         static_for<STAGES - 1>([&](auto S) {
             plan_loads(decltype(S)::value < total);
@@ -801,7 +884,10 @@ static hipError_t launch_tile(const GemmArgs& a, const GemmConfig& c)
     X(9, 128, 128, 2, 2, 4, 0)   \
     X(10, 128, 128, 2, 2, 2, 0)  \
     X(11, 256, 128, 4, 2, 2, 1)  \
-    X(12, 128, 256, 2, 4, 2, 1)
+    X(12, 128, 256, 2, 4, 2, 1)  \
+    X(13, 256, 128, 4, 2, 3, 2)  \
+    X(14, 128, 256, 2, 4, 3, 2)  \
+    X(15, 256, 128, 2, 2, 3, 2)
 
 const VariantInfo* variant_info(int v)
 {

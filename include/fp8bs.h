@@ -183,7 +183,8 @@ enum { FP8BS_ROUTE_BS = 0, FP8BS_ROUTE_MX = 1, FP8BS_ROUTE_PT = 2 };
 typedef struct {
     int block_m;     /* rows of C per workgroup tile                                           */
     int block_n;     /* columns of C per workgroup tile (N must be a multiple)                 */
-    int waves_m;     /* wave grid inside the workgroup: waves_m x waves_n waves of 64 lanes    */
+    int waves_m;     /* wave grid inside the workgroup: waves_m x waves_n waves of 64 lanes    *
+                      * that compute (plus 4 loading waves with schedule 2)                    */
     int waves_n;
     int stages;      /* LDS buffers in the load ring (prefetch depth stages-1 K blocks)        */
     int group_m;     /* tile rows walked together by consecutive tiles (>= 1)                  */
@@ -191,8 +192,10 @@ typedef struct {
                       * 1 each XCD a contiguous eighth of all tiles, 2 each XCD a contiguous   *
                       * eighth of every set of tiles resident at the same time                 */
     int persistent;  /* 1: one workgroup per CU slot walks several tiles; 0: one per tile      */
-    int pingpong;    /* 1: the two halves of an 8-wave workgroup alternate, one running its    *
-                      * matrix instructions while the other reads its next operands (2 stages) */
+    int pingpong;    /* schedule. 0: every wave loads and computes; 1: the two halves of an    *
+                      * 8-wave workgroup alternate, one running its matrix instructions while  *
+                      * the other reads its next operands (2 stages); 2: warp-specialised,     *
+                      * four extra waves issue every global -> LDS load, the others compute    */
     int small_m;     /* 1: the small-M kernel (M <= 64; every other field is ignored): one      *
                       * workgroup per 16 output columns streams the weights once, its 8 waves  *
                       * split K (routes BS and PT; route MX through fp8mx_gemm_small_m)         */

@@ -26,7 +26,8 @@ every input already resident in HBM. Prints ONE JSON line on stdout:
                   each workload: hot and cold time, algorithmic GB/s and fraction of the HBM
                   peak of the cold launch, the small-M kernel beside the main kernel
   cpu_baseline -- the CPU oracle (fp64, OpenMP) on a bounded sample of output rows
-  parity       -- sampled rows/columns of the timed output against the oracle
+  parity       -- sampled whole rows and columns of every timed output against the oracle
+                  (16 + 16 for the main workload, 8 + 8 elsewhere)
 
 The GPU raises its clock over the first ~20 ms of sustained work, so every measurement is
 preceded by a warmup of that order (the default --warmup covers it for the main workload).
@@ -226,6 +227,9 @@ def sampled_parity(case: Case, nrows: int = 16, ncols: int = 16) -> dict:
     if case.route == "bs":
         _, r1 = o.bs_gemm(h.A, h.a_scale, h.B, h.b_scale, rows=rows)
         _, r2 = o.bs_gemm(h.A, h.a_scale, h.B, h.b_scale, cols=cols)
+    elif case.route == "pt":
+        _, r1 = o.pt_gemm(h.A, h.a_scale, h.B, h.b_scale, rows=rows)
+        _, r2 = o.pt_gemm(h.A, h.a_scale, h.B, h.b_scale, cols=cols)
     else:
         _, r1 = o.mx_gemm(h.A, h.a_e8m0, h.B, h.b_e8m0, rows=rows)
         _, r2 = o.mx_gemm(h.A, h.a_e8m0, h.B, h.b_e8m0, cols=cols)
@@ -262,7 +266,18 @@ def cpu_baseline(case: Case, target_s: float = 12.0) -> dict:
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": o.num_threads(), "kind": "oracle",
             "sample": f"{nrows} full output rows of {case.name} ({case.M}x{case.N}x{case.K}), "
                       f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64, OpenMP",
-            "seconds": round(dt, 2), "host_cpus": os.cpu_count()}
+            "seconds": round(dt, 2), "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def committed_traffic(workload_name: str):
@@ -398,9 +413,10 @@ def main() -> int:
             row.update(cold_us=round(cold_med * 1e6, 2), cold_min_us=round(cold_min * 1e6, 2),
                        cold_tflops=round(case.flops / cold_med / 1e12, 1))
             log(f"[bench] {name}: {row}")
+            # the timed output against the oracle on sampled whole rows and columns
+            row["parity"] = sampled_parity(case, *((16, 16) if name == MAIN else (8, 8)))
+            log(f"[bench] parity {name} {row['parity']}")
             if name == MAIN:
-                row["parity"] = sampled_parity(case)
-                log(f"[bench] parity {row['parity']}")
                 ceiling = mfma_ceiling(case, stream)
                 log(f"[bench] mfma ceiling {ceiling}")
                 baseline = None if args.no_cpu else cpu_baseline(case)
@@ -422,7 +438,8 @@ def main() -> int:
             bs_us = per_shape[name]["us"]
             twin[name] = dict(us=round(ev * 1e6, 2), tflops=round(tc.flops / ev / 1e12, 1),
                               pct_peak=round(100 * tc.flops / ev / 1e12 / PEAK_FP8_TFLOPS, 2),
-                              bs_over_twin=round(bs_us / (ev * 1e6), 3), config=tc.config)
+                              bs_over_twin=round(bs_us / (ev * 1e6), 3), config=tc.config,
+                              parity=sampled_parity(tc, 8, 8))
             log(f"[bench] twin {name}: {twin[name]}")
             tc.free()
             del tc
@@ -476,6 +493,8 @@ def main() -> int:
                            us=round(ev * 1e6, 2), cold_us=round(cold_med * 1e6, 2), bytes=nb,
                            cold_gbs=round(nb / cold_med / 1e9, 1),
                            cold_frac_hbm=round(nb / cold_med / 1e9 / PEAK_HBM_GBS, 3))
+                torch.cuda.synchronize()  # the selected kernel's output, checked against the oracle
+                row["parity"] = sampled_parity(dc, min(rows, 8), 8)
                 if dc.route == "bs":
                     main_cfg = fb.Config(256, 128, 4, 2, 3, 4, 1, 1, 0) if dc.N // 128 >= 256 else \
                         fb.Config(128, 128, 2, 2, 3, 4, 1, 1, 0)
@@ -521,6 +540,8 @@ def main() -> int:
         "ceiling_twin": twin,
         "quantiser": quant,
         "small_m": small,
+        "parity_all_passed": all(r["parity"]["passed"] for r in
+                                 list(per_shape.values()) + list(twin.values()) + list(small.values())),
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "kernel_source_sha256": kernel_source_hash()[:16]},
     }

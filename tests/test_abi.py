@@ -89,6 +89,10 @@ def test_select_config_is_shape_driven(fb):
     assert (big.block_m, big.block_n) == (256, 256) and big.xcd_remap == 1
     nn = fb.fp8bs_select_config(fb.ROUTE_BS, 4096, 2048, 7168)
     assert ((4096 + nn.block_m - 1) // nn.block_m) * (2048 // nn.block_n) >= 256
+    # narrow-N: 256x128 tiles, 8 math waves (4x2) plus the four loader waves of schedule 2
+    assert (nn.block_m, nn.block_n, nn.waves_m, nn.waves_n, nn.stages, nn.pingpong) == (256, 128, 4, 2, 3, 2)
+    nn16 = fb.fp8bs_select_config(fb.ROUTE_BS, 16384, 1536, 7168)
+    assert (nn16.block_m, nn16.block_n, nn16.pingpong) == (256, 128, 2)
     mx = fb.fp8bs_select_config(fb.ROUTE_MX, 128, 192, 256)
     assert 192 % mx.block_n == 0
     wide = fb.fp8bs_select_config(fb.ROUTE_BS, 4096, 65536, 1536)  # 1024-tile bands: round-local order

@@ -295,13 +295,65 @@ def committed_traffic(workload_name: str):
 
 # ---- rocprofv3 helpers -----------------------------------------------------------------------
 
+class QuantCase:
+    """The activation quantiser of one route on bf16 N(0,1) activations of a workload's [M, K]."""
+
+    def __init__(self, route: str, name: str, stream):
+        import torch
+
+        import fp8_block_scaled_e4m3_amd as fb
+        import workload
+        cfg = workload.CONFIGS[name]
+        M, K = cfg["M"], cfg["K"]
+        g = torch.Generator(device="cuda:0")
+        g.manual_seed(0)
+        self.x = torch.randn((M, K), generator=g, device="cuda:0").to(torch.bfloat16)
+        self.A = torch.empty((M, K), dtype=torch.uint8, device="cuda:0")
+        if route == "bs":
+            self.S = torch.empty((K // 128, M), dtype=torch.float32, device="cuda:0")
+            self.launch = lambda: fb.fp8bs_quantize_act(self.x, self.A, self.S, stream)
+        else:
+            self.S = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda:0")
+            self.launch = lambda: fb.fp8mx_quantize_act(self.x, self.A, self.S, stream)
+        self.config = {"route": route, "M": M, "K": K, "input": "bf16"}
+        self.time_launches = lambda steps, warmup, st: Case.time_launches(self, steps, warmup, st)
+
+
+# --profile NAME: a GEMM workload, "quant_bs:<workload>" / "quant_mx:<workload>" (the quantiser on
+# that workload's activation shape) or "small_m:<workload>:<rows>" (the small-M kernel, or the
+# kernel the library selects, with that many activation rows against the workload's weights).
+PROFILE_KERNELS = {"gemm": ("gemm_kernel", ["gemm.hip", "device.hpp", "prep.hip"]),
+                   "quant": ("quantize_", ["quant.hip", "device.hpp"]),
+                   "small_m": ("decode_kernel", ["decode.hip", "device.hpp", "prep.hip"])}
+
+
+def profile_kind(name: str) -> str:
+    return "quant" if name.startswith("quant_") else "small_m" if name.startswith("small_m:") else "gemm"
+
+
+def source_hash(files) -> str:
+    h = hashlib.sha256()
+    for name in files:
+        with open(os.path.join(ROOT, "fp8_block_scaled_e4m3_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def profile_mode(name: str, steps: int, warmup: int) -> int:
     """Launch one workload `steps` times after `warmup`, then one device copy of COPY_BYTES
     (the byte counters of that copy calibrate FETCH_SIZE / WRITE_SIZE)."""
     import torch
     stream = torch.cuda.Stream()
+    kind = profile_kind(name)
     with torch.cuda.stream(stream):
-        case = Case(name, 0, stream)
+        if kind == "quant":
+            route, wl = name[len("quant_"):].split(":")
+            case = QuantCase(route, wl, stream)
+        elif kind == "small_m":
+            _, wl, rows = name.split(":")
+            case = Case(wl, 0, stream, rows=int(rows))
+        else:
+            case = Case(name, 0, stream)
         wall, ev = case.time_launches(steps, warmup, stream)
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
         dst = torch.empty_like(src)
@@ -310,7 +362,8 @@ def profile_mode(name: str, steps: int, warmup: int) -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
     print(json.dumps({"profile": name, "steps": steps, "warmup": warmup, "avg_launch_us": round(ev * 1e6, 2),
-                      "copy_bytes": COPY_BYTES, "config": case.config}), flush=True)
+                      "copy_bytes": COPY_BYTES, "config": case.config,
+                      "kernel_match": PROFILE_KERNELS[kind][0]}), flush=True)
     return 0
 
 
@@ -320,6 +373,7 @@ def ingest_counters(dirs: list[str]) -> int:
     known size, and record per-launch HBM traffic in profiles/traffic.json."""
     per_counter = {}
     workload_name = None
+    match = "gemm_kernel"
     for d in dirs:
         for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             with open(path) as f:
@@ -333,13 +387,15 @@ def ingest_counters(dirs: list[str]) -> int:
                 per_counter.setdefault(name, {}).setdefault(kern, []).append(val)
         meta = os.path.join(d, "profile.json")
         if os.path.exists(meta):
-            workload_name = json.load(open(meta))["profile"]
+            m = json.load(open(meta))
+            workload_name = m["profile"]
+            match = m.get("kernel_match", match)
     if not workload_name:
         print("no profile.json (the --profile output) found next to the counter csv", file=sys.stderr)
         return 2
     out = {}
     for counter, kernels in per_counter.items():
-        gemm = [v for k, vals in kernels.items() if "gemm_kernel" in k for v in vals]
+        gemm = [v for k, vals in kernels.items() if match in k for v in vals]
         copy = [v for k, vals in kernels.items() if "copyBuffer" in k or "elementwise" in k.lower() for v in vals]
         copy = [max(copy)] if copy else []
         if not gemm or not copy:
@@ -352,7 +408,7 @@ def ingest_counters(dirs: list[str]) -> int:
         print(f"missing counters: {sorted(out)}", file=sys.stderr)
         return 2
     rec = json.load(open(TRAFFIC_RECORD)) if os.path.exists(TRAFFIC_RECORD) else {}
-    rec[workload_name] = {"kernel_source_sha256": kernel_source_hash(),
+    rec[workload_name] = {"kernel_source_sha256": source_hash(PROFILE_KERNELS[profile_kind(workload_name)][1]),
                           "traffic_bytes": round(out["FETCH_SIZE"]["bytes_per_launch"] +
                                                  out["WRITE_SIZE"]["bytes_per_launch"]),
                           "counters": out}

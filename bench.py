@@ -11,8 +11,8 @@ every input already resident in HBM. Prints ONE JSON line on stdout:
   mfma_ceiling -- the matrix core's sustained rate on this workload's own operand bytes with
                   no memory traffic (the gfx950 matrix core slows down when operand bits
                   change between instructions; this is the reachable ceiling for this data)
-  per_shape    -- steady-state ("hot", back-to-back launches) time of all five workloads
-                  (tiny, narrow-N, K-light, wide-N, mxfp8), TFLOP/s, % of peak, algorithmic
+  per_shape    -- steady-state ("hot", back-to-back launches) time of every workload
+                  in workload.CONFIGS, TFLOP/s, % of peak, algorithmic
                   HBM GB/s, and the "cold" time of single launches that each follow a 1 GiB
                   write evicting L2 and the MALL
   ceiling_twin -- the promote-free twin (fp8pt_gemm: one scale per row of A and of B, applied

@@ -66,7 +66,8 @@ def _ref(oracle, cfg, x, rows=None, cols=None):
     return oracle.mx_gemm(x.A, x.a_e8m0, x.B, x.b_e8m0, rows=rows, cols=cols)[1]
 
 
-@pytest.mark.parametrize("name", ["narrow_n", "k_light", "wide_n", "mxfp8", "narrow_n_16k"])
+@pytest.mark.parametrize("name", ["narrow_n", "k_light", "wide_n", "mxfp8", "narrow_n_16k", "mxfp8_k2048",
+                                  "wide_n_shard8"])
 def test_workload_full_seed0(fb, oracle, name):
     """Every element of C at the benchmark size, in the launch configuration the benchmark
     times (the library's own choice for the shape), seed 0."""
@@ -76,7 +77,8 @@ def test_workload_full_seed0(fb, oracle, name):
     parity(got, ref, f"{name} full C seed 0")
 
 
-@pytest.mark.parametrize("name", ["narrow_n", "k_light", "wide_n", "mxfp8", "narrow_n_16k"])
+@pytest.mark.parametrize("name", ["narrow_n", "k_light", "wide_n", "mxfp8", "narrow_n_16k", "mxfp8_k2048",
+                                  "wide_n_shard8"])
 @pytest.mark.parametrize("seed", [1, 2, 3])
 def test_workload_sampled(fb, oracle, name, seed):
     """512 whole rows and 512 whole columns of C at the benchmark size for seeds 1-3 (the

@@ -24,8 +24,9 @@ after clamping to +-448.
 
 Workloads (``CONFIGS``): the four shapes of that table (narrow-N 4096x2048x7168, K-light
 16384x7168x768, wide-N 4096x65536x1536 and the page's untuned narrow-N deep-K shape
-16384x1536x7168) plus the tiny 128x256x512 case (route BS), and the mxfp8 16384x8192x1280
-case of page "aiter PR #6370" (route MX).
+16384x1536x7168) plus the tiny 128x256x512 case and one eighth of wide-N along N
+(4096x8192x1536) (route BS), and the mxfp8 16384x8192x1280 and 16384x5120x2048 cases of page
+"aiter PR #6370" (route MX).
 """
 from __future__ import annotations
 
@@ -36,7 +37,7 @@ import torch
 
 E4M3_MAX = 448.0
 
-# The five workloads the bench and the parity tests use, as (M, N, K) and route.
+# The workloads the bench and the parity tests use, as (M, N, K) and route.
 CONFIGS = {
     "tiny": dict(M=128, N=256, K=512, route="bs"),
     "narrow_n": dict(M=4096, N=2048, K=7168, route="bs"),
@@ -45,6 +46,10 @@ CONFIGS = {
     "mxfp8": dict(M=16384, N=8192, K=1280, route="mx"),
     # a second narrow-N, deep-K shape of the same class as narrow_n, untuned on the pages
     "narrow_n_16k": dict(M=16384, N=1536, K=7168, route="bs"),
+    # the mxfp8 shape with the highest throughput on page "aiter PR #6370" (same FLOPs as mxfp8)
+    "mxfp8_k2048": dict(M=16384, N=5120, K=2048, route="mx"),
+    # one GPU's share of wide_n split eight ways along N (weights sharded, activations replicated)
+    "wide_n_shard8": dict(M=4096, N=8192, K=1536, route="bs"),
 }
 
 

@@ -67,3 +67,22 @@ def test_python_wrapper_raises(fb):
     A, sa, B, sb, C = _bufs(128, 128, 256)
     with pytest.raises(fb.Fp8bsError):
         fb.fp8bs_gemm(A, sa, B, sb, torch.empty((128, 100), dtype=torch.bfloat16, device=A.device))
+
+
+def test_zero_rows_is_noop_every_route(fb):
+    """M = 0 is valid for every GEMM entry point: nothing is launched and C is untouched."""
+    d = torch.device("cuda:0")
+    A = torch.zeros((64, 256), dtype=torch.uint8, device=d)
+    buf = torch.zeros(1 << 16, dtype=torch.uint8, device=d)
+    fbuf = torch.ones(1 << 14, dtype=torch.float32, device=d)
+    C = torch.full((64, 256), 7.0, dtype=torch.bfloat16, device=d)
+    L = fb.lib
+    assert L.fp8mx_gemm(A.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), C.data_ptr(), 0, 256, 256,
+                        None) == 0
+    assert L.fp8pt_gemm(A.data_ptr(), fbuf.data_ptr(), buf.data_ptr(), fbuf.data_ptr(), C.data_ptr(), 0, 256, 256,
+                        None) == 0
+    assert L.fp8mx_gemm_small_m(A.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), C.data_ptr(), 0, 256,
+                                256, None) == 0
+    assert L.fp8mx_quantize_act(fbuf.data_ptr(), 0, A.data_ptr(), buf.data_ptr(), 0, 256, None) == 0
+    torch.cuda.synchronize()
+    assert torch.all(C == 7.0) and torch.all(A == 0)

@@ -324,7 +324,7 @@ class QuantCase:
 # kernel the library selects, with that many activation rows against the workload's weights).
 PROFILE_KERNELS = {"gemm": ("gemm_kernel", ["gemm.hip", "device.hpp", "prep.hip"]),
                    "quant": ("quantize_", ["quant.hip", "device.hpp"]),
-                   "small_m": ("decode_kernel", ["decode.hip", "device.hpp", "prep.hip"])}
+                   "small_m": ("decode_", ["decode.hip", "device.hpp", "prep.hip"])}
 
 
 def profile_kind(name: str) -> str:

@@ -82,7 +82,7 @@ fp8bs_config small_m_config()
 {
     fp8bs_config c;
     memset(&c, 0, sizeof(c));
-    c.small_m = 1;
+    c.small_m = fp8bs::kDecodeAuto;
     return c;
 }
 
@@ -153,12 +153,12 @@ int run(int route, const void* A, const void* a_scale, const void* B_prep, const
         int M, int N, int K, const fp8bs_config* cfg, hipStream_t stream)
 {
     fp8bs::GemmArgs args{A, a_scale, B_prep, b_scale, C, M, N, K, stream};
-    if (cfg && cfg->small_m == 1) {
+    if (cfg && cfg->small_m >= fp8bs::kDecodeAuto && cfg->small_m <= fp8bs::kDecodeLds) {
         // the small-M kernel reads the activation scales of route MX row-major, so the packed
         // route-MX entry points cannot use it (fp8mx_gemm_small_m does)
         if (route == fp8bs::kRouteMX || M > fp8bs::kDecodeMaxRows)
             return FP8BS_E_CONFIG;
-        return hip_status(fp8bs::launch_decode(route, args));
+        return hip_status(fp8bs::launch_decode(route, args, cfg->small_m));
     }
     fp8bs::GemmConfig gc;
     int st = check_config(route, cfg, N, &gc);
@@ -399,7 +399,7 @@ int fp8mx_gemm_small_m(const void* A, const void* a_e8m0, const void* B_prep, co
     if (!aligned(A, 16) || !aligned(B_prep, 16) || !aligned(C, 16) || !aligned(b_scale_packed, 16))
         return FP8BS_E_ALIGN;
     fp8bs::GemmArgs args{A, a_e8m0, B_prep, b_scale_packed, C, M, N, K, stream};
-    return hip_status(fp8bs::launch_decode(fp8bs::kRouteMX, args));
+    return hip_status(fp8bs::launch_decode(fp8bs::kRouteMX, args, fp8bs::kDecodeAuto));
 }
 
 int fp8bs_mfma_ceiling(const void* A, const void* B_prep, int M, int N, int K, int iters, float* sink, int sink_len,

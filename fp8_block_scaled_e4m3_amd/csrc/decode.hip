@@ -4,12 +4,22 @@
 //
 // With so few rows the GEMM is bound by reading B (N*K bytes) and a 128-row output tile would
 // leave most of every matrix instruction idle, so the work is cut the other way: a workgroup
-// of 8 waves owns one 16-row sub-tile of the prepared weights (16 output columns), the 8 waves
-// split the K blocks between them, and each wave loads its fragments straight from global
-// memory into registers (no LDS staging: every weight byte is used once). Each wave keeps an
-// M x 16 partial sum (per K block: one matrix instruction per 16 activation rows, then the
-// route's scaling); the 8 partials are added through LDS in a fixed order, so results are
-// deterministic run to run. Routes:
+// owns one 16-row sub-tile of the prepared weights (16 output columns), its waves split the K
+// blocks between them, and each wave keeps an M x 16 partial sum (per K block: one matrix
+// instruction per 16 activation rows, then the route's scaling); the partials are added
+// through LDS in a fixed order, so results are deterministic run to run. Two variants:
+//  * direct: each wave loads its fragments straight from global memory into registers (16
+//    bytes per lane, 64 contiguous bytes of each of 16 rows per instruction). Cheapest when
+//    the activations are few (M <= 4) and a wave owns one or two K blocks.
+//  * LDS-staged: each wave copies its K block's activation rows, weight rows and scales into a
+//    double-buffered LDS region of its own with direct-to-LDS loads of whole 128-byte row
+//    segments (8 rows per instruction, 16-byte chunks XOR-swizzled by (row >> 1) & 7), the next
+//    block's copy in flight while the current one is computed; fragments are then read from
+//    LDS. Every workgroup re-reads all M x K activation bytes (L2 hits), and whole-line loads
+//    move them about twice as fast as the direct variant's half-line ones (measured: M = 64
+//    against 2048 x 7168 weights 17.8 -> 7.3 us). No wave reads another wave's buffer, so
+//    only the wave's own vmcnt is waited for.
+// Routes:
 //  * BS: unscaled instruction + promote acc += p * (a_s[kb, m] * b_s[n/128, kb]);
 //  * MX: scaled instruction, activation exponents read row-major from a_e8m0 [M, K/32], weight
 //    exponents from the packed buffer of fp8mx_prep_weights;
@@ -35,7 +45,7 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* base, size_t row, int K,
 
 template <int ROUTE, int SI>
 __global__ void __launch_bounds__(kDecodeWaves * 64)
-decode_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale, const uint8_t* __restrict__ B,
+decode_direct_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale, const uint8_t* __restrict__ B,
               const void* __restrict__ b_scale, uint16_t* __restrict__ C, int M, int N, int K)
 {
     __shared__ v4f red[kDecodeWaves][SI][64];
@@ -117,29 +127,226 @@ decode_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale, c
     }
 }
 
-template <int ROUTE>
-hipError_t launch_route(int si, const GemmArgs& a)
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ v4i dbuf_desc(const void* base)
 {
-    const dim3 grid(a.N / 16), block(kDecodeWaves * 64);
+    const uint64_t a = (uint64_t)base;
+    return v4i{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), 0x7FFFFFFF, 0x00020000};
+}
+
+template <int BYTES>
+__device__ __forceinline__ void dma(const v4i& rs, uint32_t dst, int voff, int soff)
+{
+    if constexpr (BYTES == 16)
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                     :
+                     : "s"(dst), "v"(voff), "s"(rs), "s"(soff)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+                     :
+                     : "s"(dst), "v"(voff), "s"(rs), "s"(soff)
+                     : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ uint32_t swz(uint32_t row) { return (row >> 1) & 7u; }
+
+// Per-wave LDS buffer of one K block: [A: 16*SI rows x 128 B][B: 16 rows x 128 B][scales 512 B]
+template <int ROUTE, int SI>
+struct DBuf {
+    static constexpr int kA = 16 * SI * 128;
+    static constexpr int kB = 16 * 128;
+    static constexpr int kS = ROUTE == kRoutePT ? 0 : 512;
+    static constexpr int kBytes = kA + kB + kS;
+    static constexpr int kLoads = 2 * SI + 2 + (ROUTE == kRoutePT ? 0 : 2);
+};
+
+template <int SI>
+constexpr int waves_for() { return SI == 4 ? 7 : kDecodeWaves; }  // LDS: two buffers per wave
+
+template <int ROUTE, int SI>
+__global__ void __launch_bounds__(waves_for<SI>() * 64)
+decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale, const uint8_t* __restrict__ B,
+              const void* __restrict__ b_scale, uint16_t* __restrict__ C, int M, int N, int K)
+{
+    using D = DBuf<ROUTE, SI>;
+    constexpr int NW = waves_for<SI>();
+    static_assert(2 * NW * D::kBytes <= 160 * 1024, "LDS");
+    static_assert(NW * SI * 64 * 16 <= 2 * NW * D::kBytes, "reduction fits the operand buffers");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NW * D::kBytes];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int i = lane & 15, q = lane >> 4;
+    const int jt = blockIdx.x;
+    const int KB = K >> 7;
+    const int kb0 = (wave * KB) / NW, kb1 = ((wave + 1) * KB) / NW;
+    const v4i rsA = dbuf_desc(A), rsB = dbuf_desc(B), rsSA = dbuf_desc(a_scale), rsSB = dbuf_desc(b_scale);
+    uint8_t* mybuf = lds + wave * 2 * D::kBytes;
+
+    // DMA lane offsets (without the K block term): A group g covers rows 8g..8g+7 (clamped to
+    // M-1), B group g rows 8g..8g+7 of the sub-tile; lane l -> row l/8, physical chunk l%8
+    // holding logical chunk (l%8) ^ swz(row)
+    const int r8 = lane >> 3, c8 = lane & 7;
+    int voffA[2 * SI];
+#pragma unroll
+    for (int g = 0; g < 2 * SI; ++g) {
+        const int row = 8 * g + r8;
+        voffA[g] = min(row, M - 1) * K + ((c8 ^ (int)swz(row)) << 4);
+    }
+    int voffB[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+        const int row = 8 * g + r8;
+        voffB[g] = (jt * 16 + row) * K + ((c8 ^ (int)swz(row)) << 4);
+    }
+    // scales: BS a_s[kb*M + m] (lane = row m), b_s[nb*KB + kb]; MX a_e8m0 dword of row m at
+    // K block kb, packed weight dword ((kb*N/64 + window)*64 + lane)
+    int voffSA = 0, voffSB = 0;
+    if constexpr (ROUTE == kRouteBS) {
+        voffSA = min(lane, M - 1) * 4;
+        voffSB = (jt >> 3) * KB * 4;
+    } else if constexpr (ROUTE == kRouteMX) {
+        voffSA = min(lane, M - 1) * (K >> 5);
+        voffSB = ((jt >> 2) * 64 + lane) * 4;
+    }
+
+    auto issue = [&](int kb, int b) {
+        uint8_t* base = mybuf + b * D::kBytes;
+        const uint32_t sb = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)(lds_u8*)base);
+        const int koff = __builtin_amdgcn_readfirstlane(kb * 128);
+#pragma unroll
+        for (int g = 0; g < 2 * SI; ++g)
+            dma<16>(rsA, sb + g * 1024, voffA[g], koff);
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+            dma<16>(rsB, sb + D::kA + g * 1024, voffB[g], koff);
+        if constexpr (ROUTE == kRouteBS) {
+            dma<4>(rsSA, sb + D::kA + D::kB, voffSA, __builtin_amdgcn_readfirstlane(kb * M * 4));
+            dma<4>(rsSB, sb + D::kA + D::kB + 256, voffSB, __builtin_amdgcn_readfirstlane(kb * 4));
+        } else if constexpr (ROUTE == kRouteMX) {
+            dma<4>(rsSA, sb + D::kA + D::kB, voffSA, __builtin_amdgcn_readfirstlane(kb * 4));
+            dma<4>(rsSB, sb + D::kA + D::kB + 256, voffSB, __builtin_amdgcn_readfirstlane(kb * (N >> 6) * 256));
+        }
+    };
+    const uint32_t c_lo = ((q ^ swz(i)) << 4) + i * 128u;
+    const uint32_t c_hi = (((q + 4u) ^ swz(i)) << 4) + i * 128u;
+    auto frag = [&](const uint8_t* base) -> v8i {
+        const v4i lo = *(const v4i*)(base + c_lo);
+        const v4i hi = *(const v4i*)(base + c_hi);
+        return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    };
+
+    v4f acc[SI];
+#pragma unroll
+    for (int si = 0; si < SI; ++si)
+        acc[si] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    if (kb0 < kb1)
+        issue(kb0, 0);
+    for (int kb = kb0; kb < kb1; ++kb) {
+        const int b = (kb - kb0) & 1;
+        if (kb + 1 < kb1) {
+            issue(kb + 1, b ^ 1);
+            wait_vm<D::kLoads>();
+        } else {
+            wait_vm<0>();
+        }
+        asm volatile("" ::: "memory");  // the buffer's reads stay below the wait
+        const uint8_t* base = mybuf + b * D::kBytes;
+        const v8i bf = frag(base + D::kA);
+        if constexpr (ROUTE == kRouteBS) {
+            const float sb = *(const float*)(base + D::kA + D::kB + 256);
+#pragma unroll
+            for (int si = 0; si < SI; ++si) {
+                const v8i af = frag(base + si * 16 * 128);
+                const float sa = ((const float*)(base + D::kA + D::kB))[min(16 * si + i, M - 1)];
+                const v4f p = mfma_f8(bf, af, v4f{0.f, 0.f, 0.f, 0.f});
+                acc[si] += p * (sa * sb);
+            }
+        } else if constexpr (ROUTE == kRoutePT) {
+#pragma unroll
+            for (int si = 0; si < SI; ++si)
+                acc[si] = mfma_f8(bf, frag(base + si * 16 * 128), acc[si]);
+        } else {
+            const uint32_t wd = ((const uint32_t*)(base + D::kA + D::kB + 256))[lane];
+            const int sbyte = (int)((wd >> (8 * (jt & 3))) & 0xffu);
+#pragma unroll
+            for (int si = 0; si < SI; ++si) {
+                const uint32_t ad = ((const uint32_t*)(base + D::kA + D::kB))[min(16 * si + i, M - 1)];
+                const int sabyte = (int)((ad >> (8 * q)) & 0xffu);
+                acc[si] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, frag(base + si * 16 * 128), acc[si],
+                                                                          kFmtE4M3, kFmtE4M3, 0, sbyte, 0, sabyte);
+            }
+        }
+        // every read of this buffer is done before the next iteration's loads refill it
+        __builtin_amdgcn_s_waitcnt((15) | (7 << 4) | (0 << 8) | (3 << 14));
+    }
+
+    __syncthreads();  // reduction storage reuses the operand buffers
+    v4f* red = (v4f*)lds;  // [wave][si][64]
+#pragma unroll
+    for (int si = 0; si < SI; ++si)
+        red[(wave * SI + si) * 64 + lane] = acc[si];
+    __syncthreads();
+    if (wave < SI) {
+        const int si = wave;
+        v4f s = red[si * 64 + lane];
+#pragma unroll
+        for (int w = 1; w < NW; ++w)
+            s += red[(w * SI + si) * 64 + lane];
+        const int m = 16 * si + i;
+        const int n = 64 * (jt >> 2) + 32 * ((jt & 3) >> 1) + 8 * q + 4 * (jt & 1);
+        if constexpr (ROUTE == kRoutePT) {
+            const float sa = ((const float*)a_scale)[min(m, M - 1)];
+            const v4f sbv = *(const v4f*)((const float*)b_scale + n);
+            s = s * (sbv * sa);
+        }
+        if (m < M) {
+            v2i packed;
+            packed.x = (int)pack_bf16x2(s.x, s.y);
+            packed.y = (int)pack_bf16x2(s.z, s.w);
+            *(v2i*)(C + (size_t)m * N + n) = packed;
+        }
+    }
+}
+
+template <int ROUTE, int SI>
+void launch_one(int variant, const GemmArgs& a)
+{
     const uint8_t* A = (const uint8_t*)a.A;
     const uint8_t* B = (const uint8_t*)a.B;
     uint16_t* C = (uint16_t*)a.C;
+    if (variant == kDecodeLds)
+        hipLaunchKernelGGL((decode_lds_kernel<ROUTE, SI>), dim3(a.N / 16), dim3(waves_for<SI>() * 64), 0, a.stream,
+                           A, a.a_scale, B, a.b_scale, C, a.M, a.N, a.K);
+    else
+        hipLaunchKernelGGL((decode_direct_kernel<ROUTE, SI>), dim3(a.N / 16), dim3(kDecodeWaves * 64), 0, a.stream,
+                           A, a.a_scale, B, a.b_scale, C, a.M, a.N, a.K);
+}
+
+template <int ROUTE>
+hipError_t launch_route(int si, int variant, const GemmArgs& a)
+{
     switch (si) {
     case 1:
-        hipLaunchKernelGGL((decode_kernel<ROUTE, 1>), grid, block, 0, a.stream, A, a.a_scale, B, a.b_scale, C, a.M,
-                           a.N, a.K);
+        launch_one<ROUTE, 1>(variant, a);
         break;
     case 2:
-        hipLaunchKernelGGL((decode_kernel<ROUTE, 2>), grid, block, 0, a.stream, A, a.a_scale, B, a.b_scale, C, a.M,
-                           a.N, a.K);
+        launch_one<ROUTE, 2>(variant, a);
         break;
     case 3:
-        hipLaunchKernelGGL((decode_kernel<ROUTE, 3>), grid, block, 0, a.stream, A, a.a_scale, B, a.b_scale, C, a.M,
-                           a.N, a.K);
+        launch_one<ROUTE, 3>(variant, a);
         break;
     default:
-        hipLaunchKernelGGL((decode_kernel<ROUTE, 4>), grid, block, 0, a.stream, A, a.a_scale, B, a.b_scale, C, a.M,
-                           a.N, a.K);
+        launch_one<ROUTE, 4>(variant, a);
         break;
     }
     return hipGetLastError();
@@ -147,16 +354,23 @@ hipError_t launch_route(int si, const GemmArgs& a)
 
 }  // namespace
 
-hipError_t launch_decode(int route, const GemmArgs& a)
+hipError_t launch_decode(int route, const GemmArgs& a, int variant)
 {
     if (a.M <= 0 || a.M > kDecodeMaxRows || a.N % 64 != 0 || a.K % 128 != 0)
         return hipErrorInvalidValue;
+    if (variant == kDecodeAuto) {
+        // the LDS-staged variant unless the activations are few and every wave owns at most two
+        // K blocks (there the extra LDS round trip is not repaid: 1 x 65536 x 1536 direct 16.3
+        // us, staged 18.1; 64 x 2048 x 7168 direct 17.8, staged 7.3)
+        const int blocks_per_wave = ((a.K >> 7) + kDecodeWaves - 1) / kDecodeWaves;
+        variant = (a.M > 4 || blocks_per_wave >= 3) ? kDecodeLds : kDecodeDirect;
+    }
     const int si = (a.M + 15) / 16;
     if (route == kRouteBS)
-        return launch_route<kRouteBS>(si, a);
+        return launch_route<kRouteBS>(si, variant, a);
     if (route == kRoutePT)
-        return launch_route<kRoutePT>(si, a);
-    return launch_route<kRouteMX>(si, a);
+        return launch_route<kRoutePT>(si, variant, a);
+    return launch_route<kRouteMX>(si, variant, a);
 }
 
 }  // namespace fp8bs

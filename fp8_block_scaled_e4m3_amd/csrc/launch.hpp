@@ -40,9 +40,12 @@ hipError_t launch_prep_weights(const void* B, void* B_prep, int N, int K, hipStr
 hipError_t launch_pack_scales(const void* e8m0, void* packed, int rows, int K, int permute, hipStream_t stream);
 // Small-M kernel (decode.hip): M in [1, kDecodeMaxRows], N % 64 == 0, K % 128 == 0. Route BS
 // takes a_scale [K/128, M] fp32 as the main kernel does; route MX takes the activation
-// exponents row-major, a_e8m0 [M, K/32]; route PT a_scale [M], b_scale [N].
+// exponents row-major, a_e8m0 [M, K/32]; route PT a_scale [M], b_scale [N]. Variant: kDecodeAuto
+// (chosen by shape), kDecodeDirect (fragments loaded straight into registers) or kDecodeLds
+// (operands staged through LDS by direct-to-LDS loads); all three give identical results.
 constexpr int kDecodeMaxRows = 64;
-hipError_t launch_decode(int route, const GemmArgs& a);
+constexpr int kDecodeAuto = 1, kDecodeDirect = 2, kDecodeLds = 3;
+hipError_t launch_decode(int route, const GemmArgs& a, int variant);
 
 // Activation quantiser of route kRouteBS (scales: fp32 [K/128, M]) or kRouteMX (scales: ue8m0
 // bytes [M, K/32]); x is bf16 (in_bf16 = 1) or fp32 [M, K].

@@ -196,9 +196,12 @@ typedef struct {
                       * 8-wave workgroup alternate, one running its matrix instructions while  *
                       * the other reads its next operands (2 stages); 2: warp-specialised,     *
                       * four extra waves issue every global -> LDS load, the others compute    */
-    int small_m;     /* 1: the small-M kernel (M <= 64; every other field is ignored): one      *
-                      * workgroup per 16 output columns streams the weights once, its 8 waves  *
-                      * split K (routes BS and PT; route MX through fp8mx_gemm_small_m)         */
+    int small_m;     /* non-zero: the small-M kernel (M <= 64; every other field is ignored):   *
+                      * one workgroup per 16 output columns streams the weights once, its      *
+                      * waves split K (routes BS and PT; route MX through fp8mx_gemm_small_m). *
+                      * 1: variant chosen by shape; 2: fragments loaded straight into          *
+                      * registers; 3: operands staged through LDS. Same results for all three; *
+                      * other values are rejected with FP8BS_E_CONFIG                          */
 } fp8bs_config;
 
 /* The configuration fp8bs_gemm (route FP8BS_ROUTE_BS), fp8mx_gemm (FP8BS_ROUTE_MX) or

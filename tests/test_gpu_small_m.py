@@ -1,7 +1,9 @@
 """The small-M kernel (M <= 64, the decode regime) on the GPU through the C ABI: full-C parity
-with the oracle for routes BS, PT and MX over row counts that fill 1 to 4 sixteen-row blocks
-(ragged included) and K ranges that leave some of the 8 waves without K blocks; bit-exact on
-integer operands; the plain entry points pick it by shape; errors are rejected."""
+with the oracle for routes BS, PT and MX, for both variants (fragments loaded straight into
+registers, operands staged through LDS), over row counts that fill 1 to 4 sixteen-row blocks
+(ragged included) and K ranges that leave some waves without K blocks; the two variants agree
+bit for bit where they split K the same way; bit-exact on integer operands; the plain entry
+points pick the kernel by shape; errors are rejected."""
 import numpy as np
 import pytest
 import torch
@@ -18,14 +20,17 @@ def fb():
     return fb
 
 
-def _small(fb):
+AUTO, DIRECT, LDS = 1, 2, 3
+
+
+def _small(fb, variant=AUTO):
     c = fb.Config()
-    c.small_m = 1
+    c.small_m = variant
     return c
 
 
 SHAPES = [(1, 128, 128), (5, 256, 256), (16, 384, 1024), (17, 512, 896), (33, 192, 2048), (64, 1024, 7168),
-          (40, 4096, 384)]
+          (40, 4096, 384), (2, 192, 4096), (3, 512, 2048), (49, 256, 1408)]
 
 
 def _run_bs_cfg(fb, x, cfg):
@@ -36,22 +41,36 @@ def _run_bs_cfg(fb, x, cfg):
     return bits(C)
 
 
+@pytest.mark.parametrize("variant", [DIRECT, LDS])
 @pytest.mark.parametrize("M,N,K", [s for s in SHAPES if s[1] % 128 == 0])
-def test_small_m_bs(fb, oracle, M, N, K):
+def test_small_m_bs(fb, oracle, M, N, K, variant):
     x = workload.bs_inputs(M, N, K, M + N)
-    got = _run_bs_cfg(fb, x, _small(fb))
+    got = _run_bs_cfg(fb, x, _small(fb, variant))
     _, ref = oracle.bs_gemm(x.A, x.a_scale, x.B, x.b_scale)
-    parity(got, ref, f"small-M bs {M}x{N}x{K}")
-    again = _run_bs_cfg(fb, x, _small(fb))
-    assert np.array_equal(got, again)  # deterministic: fixed-order sum of the 8 partials
+    parity(got, ref, f"small-M bs {M}x{N}x{K} variant {variant}")
+    again = _run_bs_cfg(fb, x, _small(fb, variant))
+    assert np.array_equal(got, again)  # deterministic: fixed-order sum of the wave partials
 
 
+@pytest.mark.parametrize("variant", [DIRECT, LDS])
 @pytest.mark.parametrize("M,N,K", SHAPES)
-def test_small_m_pt(fb, oracle, M, N, K):
+def test_small_m_pt(fb, oracle, M, N, K, variant):
     z = workload.pt_inputs(M, N, K, M * 7 + N)
-    got = run_pt(fb, z, _small(fb))
+    got = run_pt(fb, z, _small(fb, variant))
     _, ref = oracle.pt_gemm(z.A, z.a_scale, z.B, z.b_scale)
-    parity(got, ref, f"small-M pt {M}x{N}x{K}")
+    parity(got, ref, f"small-M pt {M}x{N}x{K} variant {variant}")
+
+
+@pytest.mark.parametrize("M,N,K", [s for s in SHAPES if s[1] % 128 == 0 and s[0] <= 48])
+def test_small_m_variants_bitwise_equal(fb, M, N, K):
+    """Up to 48 rows both variants give each of 8 waves the same K blocks and do the same
+    arithmetic per block, so they agree bit for bit (with 49-64 rows the LDS-staged variant
+    runs 7 waves and sums in another order); the shape-chosen variant is one of the two."""
+    x = workload.bs_inputs(M, N, K, 5 * M + K)
+    direct = _run_bs_cfg(fb, x, _small(fb, DIRECT))
+    staged = _run_bs_cfg(fb, x, _small(fb, LDS))
+    assert np.array_equal(direct, staged), f"{int((direct != staged).sum())} differ"
+    assert np.array_equal(_run_bs_cfg(fb, x, _small(fb, AUTO)), direct)
 
 
 @pytest.mark.parametrize("M,N,K", [s for s in SHAPES if s[2] >= 256])
@@ -65,8 +84,9 @@ def test_small_m_mx(fb, oracle, M, N, K):
     parity(bits(C), ref, f"small-M mx {M}x{N}x{K}")
 
 
-@pytest.mark.parametrize("M,K", [(7, 512), (48, 1280)])
-def test_small_m_integer_exact(fb, oracle, M, K):
+@pytest.mark.parametrize("variant", [DIRECT, LDS])
+@pytest.mark.parametrize("M,K", [(7, 512), (48, 1280), (64, 3072)])
+def test_small_m_integer_exact(fb, oracle, M, K, variant):
     """Small-integer codes with power-of-two scales: every partial and the fixed-order sum of
     the wave partials are exact in fp32, so the output equals the oracle bit for bit."""
     N = 256
@@ -76,7 +96,7 @@ def test_small_m_integer_exact(fb, oracle, M, K):
     sa = np.exp2(rng.integers(-3, 4, size=(M, K // 128))).astype(np.float32)
     sb = np.exp2(rng.integers(-3, 4, size=(N // 128, K // 128))).astype(np.float32)
     x = workload.BSInputs(M, N, K, A, sa, B, sb)
-    got = _run_bs_cfg(fb, x, _small(fb))
+    got = _run_bs_cfg(fb, x, _small(fb, variant))
     _, ref = oracle.bs_gemm(A, sa, B, sb)
     assert np.array_equal(got, ref)
 
@@ -97,9 +117,15 @@ def test_plain_entry_picks_small_m(fb, oracle):
 
 def test_small_m_rejects(fb):
     x = workload.bs_inputs(65, 256, 256, 0)
-    with pytest.raises(fb.Fp8bsError) as e:
-        _run_bs_cfg(fb, x, _small(fb))
-    assert e.value.status == 4
+    for variant in (AUTO, DIRECT, LDS):
+        with pytest.raises(fb.Fp8bsError) as e:
+            _run_bs_cfg(fb, x, _small(fb, variant))
+        assert e.value.status == 4
+    y = workload.bs_inputs(8, 256, 256, 0)
+    for variant in (-1, 4):  # no such variant
+        with pytest.raises(fb.Fp8bsError) as e:
+            _run_bs_cfg(fb, y, _small(fb, variant))
+        assert e.value.status == 4
     d = dev()
     A = torch.zeros((65, 256), dtype=torch.uint8, device=d)
     buf = torch.zeros(1 << 16, dtype=torch.uint8, device=d)

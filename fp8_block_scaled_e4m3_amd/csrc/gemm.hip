@@ -52,6 +52,16 @@ namespace fp8bs {
 
 __device__ __forceinline__ uint32_t swz(uint32_t row) { return (row >> 1) & 7u; }
 
+// The software promote acc + p * s, one fused multiply-add per component (one rounding), spelled
+// out so that every schedule rounds the same way whatever the optimiser hoists or shares.
+__device__ __forceinline__ void promote_fma(v4f& acc, const v4f& p, float s)
+{
+    acc.x = __builtin_fmaf(p.x, s, acc.x);
+    acc.y = __builtin_fmaf(p.y, s, acc.y);
+    acc.z = __builtin_fmaf(p.z, s, acc.z);
+    acc.w = __builtin_fmaf(p.w, s, acc.w);
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -451,7 +461,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
         }
         auto promote = [&](auto Tc) {
             constexpr int t = decltype(Tc)::value;
-            acc[t / T::SJ][t % T::SJ] += p[t % 3] * srow[t / T::SJ];
+            promote_fma(acc[t / T::SJ][t % T::SJ], p[t % 3], srow[t / T::SJ]);
         };
         static_for<T::SI>([&](auto I) {
             constexpr int i = decltype(I)::value;
@@ -632,7 +642,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
             constexpr int o = t / NH, h = t % NH;
             constexpr int i = kStreamA ? o : h;
             constexpr int j = kStreamA ? h : o;
-            acc[i][j] += p[t % 3] * srow[i];
+            promote_fma(acc[i][j], p[t % 3], srow[i]);
         };
         static_for<NO>([&](auto O) {
             constexpr int o = decltype(O)::value;

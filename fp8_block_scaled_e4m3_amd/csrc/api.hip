@@ -109,17 +109,27 @@ fp8bs_config select(int route, int M, int N, int K)
         return make_config(variant, group_m, xcd, 1);
     };
     // Small M (the decode regime): the small-M kernel streams the weights once at close to
-    // HBM bandwidth; it wins for M <= 16 and, up to 64 rows, whenever the main kernel's tiles
-    // would not fill the CUs (measured: 7168 x 7168 weights, M = 1: 10.2 vs 37.6 us; with
-    // 65536 x 1536 weights the main kernel is faster from M = 32). Route MX reads its packed
-    // activation scales only in the main kernel (fp8mx_gemm_small_m is its small-M entry).
+    // HBM bandwidth. It wins whenever the main kernel's one row of tiles would not fill the CUs
+    // (measured: 7168 x 7168 weights, M = 1: 9.1 vs 37.5 us, M = 64: 16.5 vs 37.6 us), and for
+    // M <= 4 everywhere; from M = 5 to 16 it loses where a row of 128 x 256 tiles already fills
+    // the CUs (65536 x 1536 weights, M = 8 and 16: 18.5 vs 17.5 us), above 16 rows wherever a
+    // row of 128 x 128 tiles does (M = 64: 65536 x 1536 43.8 vs 18.9 us, 32768 x 1536 22.3 vs
+    // 11.5 us, 32768 x 7168 61.6 vs 39.7 us). Route MX reads its packed activation scales
+    // only in the main kernel (fp8mx_gemm_small_m is its small-M entry).
     if (route != fp8bs::kRouteMX && M >= 1 && M <= fp8bs::kDecodeMaxRows) {
-        const int bm = 256, bn = N % 128 == 0 ? 128 : 64;
-        if (M <= 16 || ((M + bm - 1) / bm) * (N / bn) < kCUs)
+        const bool row_fills_128x256 = N % 256 == 0 && N / 256 >= kCUs;
+        const bool row_fills_128x128 = N / (N % 128 == 0 ? 128 : 64) >= kCUs;
+        if (M <= 4 || (M <= 16 ? !row_fills_128x256 : !row_fills_128x128))
             return small_m_config();
     }
     if ((route == fp8bs::kRouteMX || route == fp8bs::kRoutePT) && N % 128 != 0)
         return cfg(7, 64);
+    // when one row of 128-row tiles covers M, 256-row tiles would only add padding: 128 x 256
+    // (warp-specialised) where those fill the CUs, else 128 x 128 (M = 64: 65536 x 1536 weights
+    // 18.9 us against 27 us with 256 x 128 tiles; 32768 x 1536 11.5 against 15.3 us; 32768 x
+    // 7168 39.7 against 55.3 us)
+    if (M <= 128)
+        return N % 256 == 0 && tiles(128, 256) >= kCUs ? cfg(14, 256) : cfg(0, 128);
     if (N % 256 == 0 && tiles(256, 256) >= 2 * kCUs)
         return cfg(2, 256);
     // the 256x128 / 128x256 tiles run warp-specialised (four loader waves beside the eight

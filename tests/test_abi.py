@@ -101,9 +101,12 @@ def test_select_config_is_shape_driven(fb):
                          (fb.ROUTE_BS, (128, 256, 512)), (fb.ROUTE_BS, (1, 128, 128))):
         c = fb.fp8bs_select_config(route, *shape)
         assert c.small_m == 1 or (shape[1] % c.block_n == 0 and c.group_m >= 1)
-    # few rows (the decode regime): the small-M kernel for routes BS and PT when M <= 16, or up
-    # to 64 rows while the main kernel's 256x128 tiles would not fill the 256 CUs
-    for route, shape, small in ((fb.ROUTE_BS, (1, 128, 128), 1), (fb.ROUTE_BS, (16, 65536, 1536), 1),
+    # few rows (the decode regime): the small-M kernel for routes BS and PT when M <= 4, up to
+    # 16 rows unless one row of 128x256 tiles fills the 256 CUs, up to 64 rows unless one row of
+    # 128x128 tiles does
+    for route, shape, small in ((fb.ROUTE_BS, (1, 128, 128), 1), (fb.ROUTE_BS, (4, 65536, 1536), 1),
+                                (fb.ROUTE_BS, (16, 65536, 1536), 0), (fb.ROUTE_BS, (16, 32768, 1536), 1),
+                                (fb.ROUTE_BS, (17, 32768, 1536), 0), (fb.ROUTE_BS, (64, 16384, 1536), 1),
                                 (fb.ROUTE_BS, (64, 2048, 7168), 1), (fb.ROUTE_BS, (64, 65536, 1536), 0),
                                 (fb.ROUTE_BS, (65, 128, 7168), 0), (fb.ROUTE_PT, (33, 4096, 512), 1),
                                 (fb.ROUTE_PT, (0, 4096, 512), 0), (fb.ROUTE_MX, (64, 4096, 512), 0)):
@@ -111,6 +114,18 @@ def test_select_config_is_shape_driven(fb):
         assert c.small_m == small, (route, shape)
         if small:
             assert (c.block_m, c.block_n, c.stages) == (0, 0, 0)
+    # one row of 128-row tiles covers M and fills the CUs: the 128x256 warp-specialised tile
+    for route, shape in ((fb.ROUTE_BS, (16, 65536, 1536)), (fb.ROUTE_BS, (128, 65536, 1536)),
+                         (fb.ROUTE_PT, (64, 65536, 7168)), (fb.ROUTE_MX, (64, 65536, 1536))):
+        c = fb.fp8bs_select_config(route, *shape)
+        assert (c.block_m, c.block_n, c.pingpong) == (128, 256, 2), (route, shape)
+    # otherwise 128x128 (one row of 128-row tiles never needs 256-row tiles)
+    for route, shape in ((fb.ROUTE_BS, (64, 32768, 1536)), (fb.ROUTE_BS, (128, 2048, 7168)),
+                         (fb.ROUTE_MX, (128, 32768, 1536)), (fb.ROUTE_PT, (100, 4096, 512))):
+        c = fb.fp8bs_select_config(route, *shape)
+        assert (c.block_m, c.block_n, c.pingpong) == (128, 128, 0), (route, shape)
+    c = fb.fp8bs_select_config(fb.ROUTE_BS, 129, 65536, 1536)
+    assert c.block_m == 256
 
 
 def test_select_config_rejects_bad_input(fb):

@@ -23,8 +23,9 @@ every input already resident in HBM. Prints ONE JSON line on stdout:
                   algorithmic traffic (2 B read + 1 B written per element, plus scales) and the
                   fraction of the 8 TB/s HBM peak
   small_m      -- few activation rows (M = 1, 16, 64: the decode regime) against the weights of
-                  each workload: hot and cold time, algorithmic GB/s and fraction of the HBM
-                  peak of the cold launch, the small-M kernel beside the main kernel
+                  each workload: hot and cold time of the plain entry point, algorithmic GB/s and
+                  fraction of the HBM peak of the cold launch; for route BS also the small-M
+                  kernel and the main kernel (128-row tile) each forced
   cpu_baseline -- the CPU oracle (fp64, OpenMP) on a bounded sample of output rows
   parity       -- sampled whole rows and columns of every timed output against the oracle
                   (16 + 16 for the main workload, 8 + 8 elsewhere)
@@ -537,7 +538,9 @@ def main() -> int:
 
         # few rows (the decode regime): the weights dominate the traffic, so the bound is HBM.
         # Hot = back-to-back launches (weights may stay in the MALL between launches), cold =
-        # single launches after a 1 GiB write; the main kernel with a fixed tile beside it.
+        # single launches after a 1 GiB write. `us` is the plain entry point (the kernel the
+        # library selects); for route BS the small-M kernel and the main kernel (with the 128-row
+        # tile the library uses when M <= 128) are each timed beside it.
         small = {}
         for wname in ("narrow_n", "k_light", "narrow_n_16k", "wide_n", "mxfp8"):
             for rows in (1, 16, 64):
@@ -552,14 +555,17 @@ def main() -> int:
                 torch.cuda.synchronize()  # the selected kernel's output, checked against the oracle
                 row["parity"] = sampled_parity(dc, min(rows, 8), 8)
                 if dc.route == "bs":
-                    main_cfg = fb.Config(256, 128, 4, 2, 3, 4, 1, 1, 0) if dc.N // 128 >= 256 else \
-                        fb.Config(128, 128, 2, 2, 3, 4, 1, 1, 0)
-                    dc.launch = lambda dc=dc, c=main_cfg: fb.fp8bs_gemm_with_config(
-                        dc.A, dc.sa, dc.B, dc.sb, dc.C, c, stream)
-                    _, evm, _ = dc.steady_state(stream, 0.03, 0.03)
-                    cold_m, _ = dc.cold(stream, scratch, reps=9)
-                    row.update(main_kernel_us=round(evm * 1e6, 2), main_kernel_cold_us=round(cold_m * 1e6, 2),
-                               main_kernel_tile=f"{main_cfg.block_m}x{main_cfg.block_n}")
+                    forced = fb.Config()
+                    forced.small_m = 1
+                    main_cfg = fb.Config(128, 256, 2, 4, 3, 4, 1, 1, 2) if dc.N % 256 == 0 and dc.N // 256 >= 256 \
+                        else fb.Config(128, 128, 2, 2, 3, 4, 1, 1, 0)
+                    for key, c in (("small_m_kernel", forced), ("main_kernel", main_cfg)):
+                        dc.launch = lambda dc=dc, c=c: fb.fp8bs_gemm_with_config(
+                            dc.A, dc.sa, dc.B, dc.sb, dc.C, c, stream)
+                        _, evm, _ = dc.steady_state(stream, 0.03, 0.03)
+                        cold_m, _ = dc.cold(stream, scratch, reps=9)
+                        row.update({f"{key}_us": round(evm * 1e6, 2), f"{key}_cold_us": round(cold_m * 1e6, 2)})
+                    row["main_kernel_tile"] = f"{main_cfg.block_m}x{main_cfg.block_n}"
                 small[f"{wname}_weights_M{rows}"] = row
                 log(f"[bench] small-M {wname} M={rows}: {row}")
                 dc.free()

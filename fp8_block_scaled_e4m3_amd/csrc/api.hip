@@ -77,6 +77,12 @@ fp8bs_config make_config(int variant, int group_m, int xcd_remap, int persistent
     return c;
 }
 
+// Rows the small-M kernel takes: chunks of kDecodeMaxRows rows, at most kDecodeMaxChunks of them.
+bool small_m_rows_ok(int M)
+{
+    return M >= 1 && (M + fp8bs::kDecodeMaxRows - 1) / fp8bs::kDecodeMaxRows <= fp8bs::kDecodeMaxChunks;
+}
+
 // The small-M kernel: the tile fields do not apply to it and are zeroed.
 fp8bs_config small_m_config()
 {
@@ -93,7 +99,6 @@ fp8bs_config small_m_config()
 // a multiple of 128).
 fp8bs_config select(int route, int M, int N, int K)
 {
-    (void)K;
     const int kCUs = 256;
     const int group_m = 4;
     auto tiles = [&](int bm, int bn) { return ((M + bm - 1) / bm) * (N / bn); };
@@ -122,6 +127,14 @@ fp8bs_config select(int route, int M, int N, int K)
         if (M <= 4 || (M <= 16 ? !row_fills_128x256 : !row_fills_128x128))
             return small_m_config();
     }
+    // More rows over deep K while the main kernel's 128-row tiles would cover at most a quarter
+    // of the CUs: the small-M kernel in 64-row chunks, each chunk streaming the weights again
+    // (2048 x 7168 weights, M = 96 to 512: 7.4-29.4 us against 38 us; 7168 x 7168, M = 128:
+    // 31.7 against 38.1 us, but M = 192: 46.6 against 38.7; over K = 768 or 1280 the main
+    // kernel wins from M = 96).
+    if (route != fp8bs::kRouteMX && M > fp8bs::kDecodeMaxRows && K >= 4096 &&
+        tiles(128, N % 128 == 0 ? 128 : 64) <= kCUs / 4 && small_m_rows_ok(M))
+        return small_m_config();
     if ((route == fp8bs::kRouteMX || route == fp8bs::kRoutePT) && N % 128 != 0)
         return cfg(7, 64);
     // when one row of 128-row tiles covers M, 256-row tiles would only add padding: 128 x 256
@@ -138,6 +151,14 @@ fp8bs_config select(int route, int M, int N, int K)
     if (tiles(256, 128) >= kCUs)
         return cfg(13, 128);
     if (N % 256 == 0 && tiles(128, 256) >= kCUs)
+        return cfg(14, 256);
+    // 128x128 tiles, unless they would need more rounds of the CUs than the larger ones (7168 x
+    // 7168 weights, M = 640: 280 tiles in two rounds, 74.6 us, against 168 tiles of 256 x 128 in
+    // one, 46.1 us)
+    auto rounds = [&](int bm, int bn) { return (tiles(bm, bn) + kCUs - 1) / kCUs; };
+    if (rounds(256, 128) < rounds(128, 128))
+        return cfg(13, 128);
+    if (N % 256 == 0 && rounds(128, 256) < rounds(128, 128))
         return cfg(14, 256);
     return cfg(0, 128);
 }
@@ -166,7 +187,7 @@ int run(int route, const void* A, const void* a_scale, const void* B_prep, const
     if (cfg && cfg->small_m >= fp8bs::kDecodeAuto && cfg->small_m <= fp8bs::kDecodeLds) {
         // the small-M kernel reads the activation scales of route MX row-major, so the packed
         // route-MX entry points cannot use it (fp8mx_gemm_small_m does)
-        if (route == fp8bs::kRouteMX || M > fp8bs::kDecodeMaxRows)
+        if (route == fp8bs::kRouteMX || !small_m_rows_ok(M))
             return FP8BS_E_CONFIG;
         return hip_status(fp8bs::launch_decode(route, args, cfg->small_m));
     }
@@ -399,7 +420,7 @@ int fp8mx_quantize_act(const void* x, int x_dtype, void* A_codes, void* a_e8m0, 
 int fp8mx_gemm_small_m(const void* A, const void* a_e8m0, const void* B_prep, const void* b_scale_packed, void* C,
                        int M, int N, int K, hipStream_t stream)
 {
-    if (M < 0 || M > fp8bs::kDecodeMaxRows || N < 64 || N % 64 != 0 || K < 256 || K % 128 != 0 ||
+    if (M < 0 || (M > 0 && !small_m_rows_ok(M)) || N < 64 || N % 64 != 0 || K < 256 || K % 128 != 0 ||
         !fits_offsets(M, N, K))
         return FP8BS_E_SHAPE;
     if (M == 0)

@@ -4,10 +4,12 @@
 //
 // With so few rows the GEMM is bound by reading B (N*K bytes) and a 128-row output tile would
 // leave most of every matrix instruction idle, so the work is cut the other way: a workgroup
-// owns one 16-row sub-tile of the prepared weights (16 output columns), its waves split the K
-// blocks between them, and each wave keeps an M x 16 partial sum (per K block: one matrix
-// instruction per 16 activation rows, then the route's scaling); the partials are added
-// through LDS in a fixed order, so results are deterministic run to run. Two variants:
+// owns one 16-row sub-tile of the prepared weights (16 output columns) and one chunk of up to
+// 64 activation rows (grid y; more rows take more chunks, each re-reading the weights, mostly
+// from L2), its waves split the K blocks between them, and each wave keeps a rows x 16 partial
+// sum (per K block: one matrix instruction per 16 activation rows, then the route's scaling);
+// the partials are added through LDS in a fixed order, so results are deterministic run to
+// run and do not depend on the chunking. Two variants:
 //  * direct: each wave loads its fragments straight from global memory into registers (16
 //    bytes per lane, 64 contiguous bytes of each of 16 rows per instruction). Cheapest when
 //    the activations are few (M <= 4) and a wave owns one or two K blocks.
@@ -53,13 +55,14 @@ decode_direct_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_s
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = lane & 15, q = lane >> 4;
     const int jt = blockIdx.x;  // 16-row sub-tile of the prepared weights
+    const int m0 = blockIdx.y * kDecodeMaxRows;  // first activation row of the chunk
     const int KB = K >> 7;
     const int kb0 = (wave * KB) / kDecodeWaves, kb1 = ((wave + 1) * KB) / kDecodeWaves;
     const size_t brow = (size_t)jt * 16 + i;
     int arow[SI];
 #pragma unroll
     for (int si = 0; si < SI; ++si)
-        arow[si] = min(16 * si + i, M - 1);  // rows past M repeat row M-1 and are not stored
+        arow[si] = min(m0 + 16 * si + i, M - 1);  // rows past M repeat row M-1 and are not stored
 
     v4f acc[SI];
 #pragma unroll
@@ -109,7 +112,7 @@ decode_direct_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_s
 #pragma unroll
         for (int w = 1; w < kDecodeWaves; ++w)
             s += red[w][si][lane];
-        const int m = 16 * si + i;
+        const int m = m0 + 16 * si + i;
         // result register r of lane group q is prepared row 16*(jt%4) + 4q + r of the 64-row
         // window, i.e. output column 64*(jt/4) + 32*((jt%4)/2) + 8q + 4*(jt%2) + r
         const int n = 64 * (jt >> 2) + 32 * ((jt & 3) >> 1) + 8 * q + 4 * (jt & 1);
@@ -186,20 +189,21 @@ decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scal
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = lane & 15, q = lane >> 4;
     const int jt = blockIdx.x;
+    const int m0 = blockIdx.y * kDecodeMaxRows;  // first activation row of the chunk
     const int KB = K >> 7;
     const int kb0 = (wave * KB) / NW, kb1 = ((wave + 1) * KB) / NW;
     const v4i rsA = dbuf_desc(A), rsB = dbuf_desc(B), rsSA = dbuf_desc(a_scale), rsSB = dbuf_desc(b_scale);
     uint8_t* mybuf = lds + wave * 2 * D::kBytes;
 
-    // DMA lane offsets (without the K block term): A group g covers rows 8g..8g+7 (clamped to
-    // M-1), B group g rows 8g..8g+7 of the sub-tile; lane l -> row l/8, physical chunk l%8
-    // holding logical chunk (l%8) ^ swz(row)
+    // DMA lane offsets (without the K block term): A group g covers rows m0+8g .. m0+8g+7
+    // (clamped to M-1), B group g rows 8g..8g+7 of the sub-tile; lane l -> row l/8, physical
+    // chunk l%8 holding logical chunk (l%8) ^ swz(row)
     const int r8 = lane >> 3, c8 = lane & 7;
     int voffA[2 * SI];
 #pragma unroll
     for (int g = 0; g < 2 * SI; ++g) {
         const int row = 8 * g + r8;
-        voffA[g] = min(row, M - 1) * K + ((c8 ^ (int)swz(row)) << 4);
+        voffA[g] = min(m0 + row, M - 1) * K + ((c8 ^ (int)swz(row)) << 4);
     }
     int voffB[2];
 #pragma unroll
@@ -207,14 +211,14 @@ decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scal
         const int row = 8 * g + r8;
         voffB[g] = (jt * 16 + row) * K + ((c8 ^ (int)swz(row)) << 4);
     }
-    // scales: BS a_s[kb*M + m] (lane = row m), b_s[nb*KB + kb]; MX a_e8m0 dword of row m at
-    // K block kb, packed weight dword ((kb*N/64 + window)*64 + lane)
+    // scales: BS a_s[kb*M + m] (lane = row m - m0), b_s[nb*KB + kb]; MX a_e8m0 dword of row m
+    // at K block kb, packed weight dword ((kb*N/64 + window)*64 + lane)
     int voffSA = 0, voffSB = 0;
     if constexpr (ROUTE == kRouteBS) {
-        voffSA = min(lane, M - 1) * 4;
+        voffSA = min(m0 + lane, M - 1) * 4;
         voffSB = (jt >> 3) * KB * 4;
     } else if constexpr (ROUTE == kRouteMX) {
-        voffSA = min(lane, M - 1) * (K >> 5);
+        voffSA = min(m0 + lane, M - 1) * (K >> 5);
         voffSB = ((jt >> 2) * 64 + lane) * 4;
     }
 
@@ -267,7 +271,7 @@ decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scal
 #pragma unroll
             for (int si = 0; si < SI; ++si) {
                 const v8i af = frag(base + si * 16 * 128);
-                const float sa = ((const float*)(base + D::kA + D::kB))[min(16 * si + i, M - 1)];
+                const float sa = ((const float*)(base + D::kA + D::kB))[16 * si + i];  // row m0+16si+i, clamped
                 const v4f p = mfma_f8(bf, af, v4f{0.f, 0.f, 0.f, 0.f});
                 acc[si] += p * (sa * sb);
             }
@@ -280,7 +284,7 @@ decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scal
             const int sbyte = (int)((wd >> (8 * (jt & 3))) & 0xffu);
 #pragma unroll
             for (int si = 0; si < SI; ++si) {
-                const uint32_t ad = ((const uint32_t*)(base + D::kA + D::kB))[min(16 * si + i, M - 1)];
+                const uint32_t ad = ((const uint32_t*)(base + D::kA + D::kB))[16 * si + i];
                 const int sabyte = (int)((ad >> (8 * q)) & 0xffu);
                 acc[si] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, frag(base + si * 16 * 128), acc[si],
                                                                           kFmtE4M3, kFmtE4M3, 0, sbyte, 0, sabyte);
@@ -302,7 +306,7 @@ decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scal
 #pragma unroll
         for (int w = 1; w < NW; ++w)
             s += red[(w * SI + si) * 64 + lane];
-        const int m = 16 * si + i;
+        const int m = m0 + 16 * si + i;
         const int n = 64 * (jt >> 2) + 32 * ((jt & 3) >> 1) + 8 * q + 4 * (jt & 1);
         if constexpr (ROUTE == kRoutePT) {
             const float sa = ((const float*)a_scale)[min(m, M - 1)];
@@ -321,14 +325,15 @@ decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scal
 template <int ROUTE, int SI>
 void launch_one(int variant, const GemmArgs& a)
 {
+    const int chunks = (a.M + kDecodeMaxRows - 1) / kDecodeMaxRows;
     const uint8_t* A = (const uint8_t*)a.A;
     const uint8_t* B = (const uint8_t*)a.B;
     uint16_t* C = (uint16_t*)a.C;
     if (variant == kDecodeLds)
-        hipLaunchKernelGGL((decode_lds_kernel<ROUTE, SI>), dim3(a.N / 16), dim3(waves_for<SI>() * 64), 0, a.stream,
+        hipLaunchKernelGGL((decode_lds_kernel<ROUTE, SI>), dim3(a.N / 16, chunks), dim3(waves_for<SI>() * 64), 0, a.stream,
                            A, a.a_scale, B, a.b_scale, C, a.M, a.N, a.K);
     else
-        hipLaunchKernelGGL((decode_direct_kernel<ROUTE, SI>), dim3(a.N / 16), dim3(kDecodeWaves * 64), 0, a.stream,
+        hipLaunchKernelGGL((decode_direct_kernel<ROUTE, SI>), dim3(a.N / 16, chunks), dim3(kDecodeWaves * 64), 0, a.stream,
                            A, a.a_scale, B, a.b_scale, C, a.M, a.N, a.K);
 }
 
@@ -356,7 +361,8 @@ hipError_t launch_route(int si, int variant, const GemmArgs& a)
 
 hipError_t launch_decode(int route, const GemmArgs& a, int variant)
 {
-    if (a.M <= 0 || a.M > kDecodeMaxRows || a.N % 64 != 0 || a.K % 128 != 0)
+    if (a.M <= 0 || (a.M + kDecodeMaxRows - 1) / kDecodeMaxRows > kDecodeMaxChunks || a.N % 64 != 0 ||
+        a.K % 128 != 0)
         return hipErrorInvalidValue;
     if (variant == kDecodeAuto) {
         // the LDS-staged variant unless the activations are few and every wave owns at most two
@@ -365,7 +371,7 @@ hipError_t launch_decode(int route, const GemmArgs& a, int variant)
         const int blocks_per_wave = ((a.K >> 7) + kDecodeWaves - 1) / kDecodeWaves;
         variant = (a.M > 4 || blocks_per_wave >= 3) ? kDecodeLds : kDecodeDirect;
     }
-    const int si = (a.M + 15) / 16;
+    const int si = (min(a.M, kDecodeMaxRows) + 15) / 16;
     if (route == kRouteBS)
         return launch_route<kRouteBS>(si, variant, a);
     if (route == kRoutePT)

@@ -38,12 +38,14 @@ hipError_t launch_mfma_ceiling(const void* A, const void* B_prep, int M, int N, 
                                int sink_len, long long* flops, hipStream_t stream);
 hipError_t launch_prep_weights(const void* B, void* B_prep, int N, int K, hipStream_t stream);
 hipError_t launch_pack_scales(const void* e8m0, void* packed, int rows, int K, int permute, hipStream_t stream);
-// Small-M kernel (decode.hip): M in [1, kDecodeMaxRows], N % 64 == 0, K % 128 == 0. Route BS
+// Small-M kernel (decode.hip): M >= 1 in chunks of kDecodeMaxRows rows (at most kDecodeMaxChunks
+// chunks: the grid's y extent), N % 64 == 0, K % 128 == 0. Route BS
 // takes a_scale [K/128, M] fp32 as the main kernel does; route MX takes the activation
 // exponents row-major, a_e8m0 [M, K/32]; route PT a_scale [M], b_scale [N]. Variant: kDecodeAuto
 // (chosen by shape), kDecodeDirect (fragments loaded straight into registers) or kDecodeLds
 // (operands staged through LDS by direct-to-LDS loads); all three give identical results.
 constexpr int kDecodeMaxRows = 64;
+constexpr int kDecodeMaxChunks = 65535;
 constexpr int kDecodeAuto = 1, kDecodeDirect = 2, kDecodeLds = 3;
 hipError_t launch_decode(int route, const GemmArgs& a, int variant);
 

@@ -162,11 +162,12 @@ int fp8mx_gemm(const void *A, const void *a_scale_packed, const void *B_prep,
 int fp8pt_gemm(const void *A, const float *a_scale, const void *B_prep, const float *b_scale,
                void *C, int M, int N, int K, hipStream_t stream);
 
-/* Route MX for M <= 64 rows (the decode regime): the small-M kernel, which streams the
- * weights once. The activation exponents are taken row-major, a_e8m0 [M, K/32] bytes (biased
- * by 127; the packed layout of fp8mx_pack_a_scale needs whole 64-row groups); B_prep and
- * b_scale_packed come from fp8mx_prep_weights. Constraints: 0 <= M <= 64, N % 64 == 0,
- * K % 128 == 0, K >= 256; A, B_prep, C and b_scale_packed 16-byte aligned. */
+/* Route MX through the small-M kernel (meant for few rows, the decode regime; it streams the
+ * weights once per 64-row chunk of A, so it also serves M that is not a multiple of 64). The
+ * activation exponents are taken row-major, a_e8m0 [M, K/32] bytes (biased by 127; the packed
+ * layout of fp8mx_pack_a_scale needs whole 64-row groups); B_prep and b_scale_packed come from
+ * fp8mx_prep_weights. Constraints: 0 <= M <= 64 * 65535, N % 64 == 0, K % 128 == 0, K >= 256;
+ * A, B_prep, C and b_scale_packed 16-byte aligned. */
 int fp8mx_gemm_small_m(const void *A, const void *a_e8m0, const void *B_prep, const void *b_scale_packed,
                        void *C, int M, int N, int K, hipStream_t stream);
 
@@ -196,9 +197,10 @@ typedef struct {
                       * 8-wave workgroup alternate, one running its matrix instructions while  *
                       * the other reads its next operands (2 stages); 2: warp-specialised,     *
                       * four extra waves issue every global -> LDS load, the others compute    */
-    int small_m;     /* non-zero: the small-M kernel (M <= 64; every other field is ignored):   *
-                      * one workgroup per 16 output columns streams the weights once, its      *
-                      * waves split K (routes BS and PT; route MX through fp8mx_gemm_small_m). *
+    int small_m;     /* non-zero: the small-M kernel (every other field is ignored): one        *
+                      * workgroup per 16 output columns and 64-row chunk of A streams the      *
+                      * weights, its waves split K (routes BS and PT, M <= 64 * 65535; route   *
+                      * MX through fp8mx_gemm_small_m).                                        *
                       * 1: variant chosen by shape; 2: fragments loaded straight into          *
                       * registers; 3: operands staged through LDS. Same results for all three; *
                       * other values are rejected with FP8BS_E_CONFIG                          */

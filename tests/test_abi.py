@@ -103,12 +103,16 @@ def test_select_config_is_shape_driven(fb):
         assert c.small_m == 1 or (shape[1] % c.block_n == 0 and c.group_m >= 1)
     # few rows (the decode regime): the small-M kernel for routes BS and PT when M <= 4, up to
     # 16 rows unless one row of 128x256 tiles fills the 256 CUs, up to 64 rows unless one row of
-    # 128x128 tiles does
+    # 128x128 tiles does; beyond 64 rows (in 64-row chunks) over K >= 4096 while 128x128 tiles
+    # would cover at most a quarter of the CUs
     for route, shape, small in ((fb.ROUTE_BS, (1, 128, 128), 1), (fb.ROUTE_BS, (4, 65536, 1536), 1),
                                 (fb.ROUTE_BS, (16, 65536, 1536), 0), (fb.ROUTE_BS, (16, 32768, 1536), 1),
                                 (fb.ROUTE_BS, (17, 32768, 1536), 0), (fb.ROUTE_BS, (64, 16384, 1536), 1),
                                 (fb.ROUTE_BS, (64, 2048, 7168), 1), (fb.ROUTE_BS, (64, 65536, 1536), 0),
-                                (fb.ROUTE_BS, (65, 128, 7168), 0), (fb.ROUTE_PT, (33, 4096, 512), 1),
+                                (fb.ROUTE_BS, (65, 128, 7168), 1), (fb.ROUTE_PT, (33, 4096, 512), 1),
+                                (fb.ROUTE_BS, (512, 2048, 7168), 1), (fb.ROUTE_PT, (96, 1536, 7168), 1),
+                                (fb.ROUTE_BS, (640, 2048, 7168), 0), (fb.ROUTE_BS, (192, 7168, 7168), 0),
+                                (fb.ROUTE_BS, (96, 7168, 768), 0), (fb.ROUTE_MX, (128, 2048, 7168), 0),
                                 (fb.ROUTE_PT, (0, 4096, 512), 0), (fb.ROUTE_MX, (64, 4096, 512), 0)):
         c = fb.fp8bs_select_config(route, *shape)
         assert c.small_m == small, (route, shape)
@@ -120,12 +124,17 @@ def test_select_config_is_shape_driven(fb):
         c = fb.fp8bs_select_config(route, *shape)
         assert (c.block_m, c.block_n, c.pingpong) == (128, 256, 2), (route, shape)
     # otherwise 128x128 (one row of 128-row tiles never needs 256-row tiles)
-    for route, shape in ((fb.ROUTE_BS, (64, 32768, 1536)), (fb.ROUTE_BS, (128, 2048, 7168)),
+    for route, shape in ((fb.ROUTE_BS, (64, 32768, 1536)), (fb.ROUTE_BS, (128, 2048, 1024)),
                          (fb.ROUTE_MX, (128, 32768, 1536)), (fb.ROUTE_PT, (100, 4096, 512))):
         c = fb.fp8bs_select_config(route, *shape)
         assert (c.block_m, c.block_n, c.pingpong) == (128, 128, 0), (route, shape)
     c = fb.fp8bs_select_config(fb.ROUTE_BS, 129, 65536, 1536)
     assert c.block_m == 256
+    # 128x128 tiles only while they need no more rounds of the CUs than 256x128 tiles
+    for shape, tile in (((640, 7168, 7168), (256, 128)), ((1024, 7168, 7168), (256, 128)),
+                        ((1024, 2048, 7168), (128, 128)), ((200, 4096, 512), (128, 128))):
+        c = fb.fp8bs_select_config(fb.ROUTE_BS, *shape)
+        assert (c.block_m, c.block_n) == tile, shape
 
 
 def test_select_config_rejects_bad_input(fb):

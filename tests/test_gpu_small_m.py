@@ -1,9 +1,10 @@
-"""The small-M kernel (M <= 64, the decode regime) on the GPU through the C ABI: full-C parity
-with the oracle for routes BS, PT and MX, for both variants (fragments loaded straight into
-registers, operands staged through LDS), over row counts that fill 1 to 4 sixteen-row blocks
-(ragged included) and K ranges that leave some waves without K blocks; the two variants agree
-bit for bit where they split K the same way; bit-exact on integer operands; the plain entry
-points pick the kernel by shape; errors are rejected."""
+"""The small-M kernel (the decode regime; 64-row chunks of A beyond 64 rows) on the GPU through
+the C ABI: full-C parity with the oracle for routes BS, PT and MX, for both variants (fragments
+loaded straight into registers, operands staged through LDS), over row counts that fill 1 to 4
+sixteen-row blocks (ragged included) and several chunks, and K ranges that leave some waves
+without K blocks; the two variants agree bit for bit where they split K the same way; chunking
+leaves every row as a call on that chunk alone computes it; bit-exact on integer operands; the
+plain entry points pick the kernel by shape; errors are rejected."""
 import numpy as np
 import pytest
 import torch
@@ -30,7 +31,8 @@ def _small(fb, variant=AUTO):
 
 
 SHAPES = [(1, 128, 128), (5, 256, 256), (16, 384, 1024), (17, 512, 896), (33, 192, 2048), (64, 1024, 7168),
-          (40, 4096, 384), (2, 192, 4096), (3, 512, 2048), (49, 256, 1408)]
+          (40, 4096, 384), (2, 192, 4096), (3, 512, 2048), (49, 256, 1408), (65, 256, 512), (100, 384, 1024),
+          (130, 512, 896), (257, 192, 1280)]
 
 
 def _run_bs_cfg(fb, x, cfg):
@@ -101,13 +103,27 @@ def test_small_m_integer_exact(fb, oracle, M, K, variant):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("variant", [DIRECT, LDS])
+def test_small_m_chunks_are_independent(fb, variant):
+    """130 rows run as three 64-row chunks (the last ragged) give bit for bit what separate
+    calls on rows 0-63, 64-127 and 128-129 give."""
+    M, N, K = 130, 512, 1024
+    x = workload.bs_inputs(M, N, K, 31)
+    whole = _run_bs_cfg(fb, x, _small(fb, variant))
+    for lo, hi in ((0, 64), (64, 128), (128, 130)):
+        part = workload.BSInputs(hi - lo, N, K, x.A[lo:hi], x.a_scale[lo:hi], x.B, x.b_scale)
+        got = _run_bs_cfg(fb, part, _small(fb, variant))
+        assert np.array_equal(got, whole[lo:hi]), (lo, hi)
+
+
 def test_plain_entry_picks_small_m(fb, oracle):
     """fp8bs_gemm and fp8pt_gemm use the small-M kernel for few rows and narrow outputs, the
     main kernel when the main kernel's tiles fill the device."""
     assert fb.fp8bs_select_config(fb.ROUTE_BS, 8, 7168, 7168).small_m == 1
     assert fb.fp8bs_select_config(fb.ROUTE_BS, 64, 2048, 7168).small_m == 1
     assert fb.fp8bs_select_config(fb.ROUTE_BS, 64, 65536, 1536).small_m == 0
-    assert fb.fp8bs_select_config(fb.ROUTE_BS, 65, 2048, 7168).small_m == 0
+    assert fb.fp8bs_select_config(fb.ROUTE_BS, 65, 2048, 7168).small_m == 1  # 64-row chunks
+    assert fb.fp8bs_select_config(fb.ROUTE_BS, 1024, 2048, 7168).small_m == 0
     assert fb.fp8bs_select_config(fb.ROUTE_PT, 1, 4096, 512).small_m == 1
     assert fb.fp8bs_select_config(fb.ROUTE_MX, 64, 4096, 512).small_m == 0
     x = workload.bs_inputs(24, 2048, 1024, 2)
@@ -116,11 +132,6 @@ def test_plain_entry_picks_small_m(fb, oracle):
 
 
 def test_small_m_rejects(fb):
-    x = workload.bs_inputs(65, 256, 256, 0)
-    for variant in (AUTO, DIRECT, LDS):
-        with pytest.raises(fb.Fp8bsError) as e:
-            _run_bs_cfg(fb, x, _small(fb, variant))
-        assert e.value.status == 4
     y = workload.bs_inputs(8, 256, 256, 0)
     for variant in (-1, 4):  # no such variant
         with pytest.raises(fb.Fp8bsError) as e:
@@ -129,9 +140,17 @@ def test_small_m_rejects(fb):
     d = dev()
     A = torch.zeros((65, 256), dtype=torch.uint8, device=d)
     buf = torch.zeros(1 << 16, dtype=torch.uint8, device=d)
+    fbuf = torch.ones(1 << 14, dtype=torch.float32, device=d)
     C = torch.full((65, 256), 3.0, dtype=torch.bfloat16, device=d)
+    # more than 65535 chunks of 64 rows: rejected before anything is launched (the small
+    # buffers are never touched)
+    too_many = 64 * 65535 + 1
+    cfg = _small(fb, AUTO)
+    import ctypes
+    assert fb.lib.fp8bs_gemm_with_config(A.data_ptr(), fbuf.data_ptr(), buf.data_ptr(), fbuf.data_ptr(),
+                                         C.data_ptr(), too_many, 256, 256, ctypes.byref(cfg), None) == 4
     assert fb.lib.fp8mx_gemm_small_m(A.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), C.data_ptr(),
-                                     65, 256, 256, None) == 2
+                                     too_many, 256, 256, None) == 2
     assert fb.lib.fp8mx_gemm_small_m(A.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), C.data_ptr(),
                                      16, 256, 128, None) == 2
     torch.cuda.synchronize()

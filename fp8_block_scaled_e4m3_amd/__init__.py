@@ -213,7 +213,8 @@ def fp8mx_quantize_act(x: torch.Tensor, A_codes: torch.Tensor, a_e8m0: torch.Ten
 
 def fp8mx_gemm_small_m(A: torch.Tensor, a_e8m0: torch.Tensor, B_prep: torch.Tensor, b_scale_packed: torch.Tensor,
                        C: torch.Tensor, stream=None) -> torch.Tensor:
-    """Route MX for M <= 64: a_e8m0 [M, K/32] uint8 row-major (not packed)."""
+    """Route MX through the small-M kernel (meant for few rows; any M): a_e8m0 [M, K/32] uint8
+    row-major (not packed)."""
     M, K = A.shape
     N = C.shape[1]
     _check("fp8mx_gemm_small_m", lib.fp8mx_gemm_small_m(_ptr(A), _ptr(a_e8m0), _ptr(B_prep), _ptr(b_scale_packed),

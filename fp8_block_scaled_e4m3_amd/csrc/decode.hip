@@ -1,4 +1,4 @@
-// decode.hip -- the small-M ("decode") regime: M <= 64 rows of activations against a weight
+// decode.hip -- the small-M ("decode") regime: few rows of activations against a weight
 // matrix streamed once from HBM (page "Flydsl Fp8 Blockscale Gemm", When to use: the decode
 // variants; page "aiter PR #6370", Not included: a separate GEMV-style kernel for M <= 32).
 //

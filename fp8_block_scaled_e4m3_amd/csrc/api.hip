@@ -119,21 +119,23 @@ fp8bs_config select(int route, int M, int N, int K)
     // M <= 4 everywhere; from M = 5 to 16 it loses where a row of 128 x 256 tiles already fills
     // the CUs (65536 x 1536 weights, M = 8 and 16: 18.5 vs 17.5 us), above 16 rows wherever a
     // row of 128 x 128 tiles does (M = 64: 65536 x 1536 43.8 vs 18.9 us, 32768 x 1536 22.3 vs
-    // 11.5 us, 32768 x 7168 61.6 vs 39.7 us). Route MX reads its packed activation scales
-    // only in the main kernel (fp8mx_gemm_small_m is its small-M entry).
-    if (route != fp8bs::kRouteMX && M >= 1 && M <= fp8bs::kDecodeMaxRows) {
+    // 11.5 us, 32768 x 7168 61.6 vs 39.7 us). Route MX (M = 64 here) the same, the kernel then
+    // reading the packed activation scales (8192 x 1280 weights: 6.1 vs 8.1 us).
+    if (M >= 1 && M <= fp8bs::kDecodeMaxRows) {
         const bool row_fills_128x256 = N % 256 == 0 && N / 256 >= kCUs;
         const bool row_fills_128x128 = N / (N % 128 == 0 ? 128 : 64) >= kCUs;
         if (M <= 4 || (M <= 16 ? !row_fills_128x256 : !row_fills_128x128))
             return small_m_config();
     }
     // More rows over deep K while the main kernel's 128-row tiles would cover at most a quarter
-    // of the CUs: the small-M kernel in 64-row chunks, each chunk streaming the weights again
-    // (2048 x 7168 weights, M = 96 to 512: 7.4-29.4 us against 38 us; 7168 x 7168, M = 128:
-    // 31.7 against 38.1 us, but M = 192: 46.6 against 38.7; over K = 768 or 1280 the main
-    // kernel wins from M = 96).
-    if (route != fp8bs::kRouteMX && M > fp8bs::kDecodeMaxRows && K >= 4096 &&
-        tiles(128, N % 128 == 0 ? 128 : 64) <= kCUs / 4 && small_m_rows_ok(M))
+    // of the CUs (an eighth for route MX, whose main kernel has no promote): the small-M kernel
+    // in 64-row chunks, each chunk streaming the weights again (2048 x 7168 weights, M = 96 to
+    // 512: 7.4-29.4 us against 38 us; 7168 x 7168, M = 128: 31.7 against 38.1 us, but M = 192:
+    // 46.6 against 38.7; over K = 768 or 1280 the main kernel wins from M = 96; route MX,
+    // 2048 x 7168, M = 256: 15.3 against 30.8 us, 7168 x 7168, M = 128: 32.0 against 31.1).
+    if (M > fp8bs::kDecodeMaxRows && K >= 4096 &&
+        tiles(128, N % 128 == 0 ? 128 : 64) <= (route == fp8bs::kRouteMX ? kCUs / 8 : kCUs / 4) &&
+        small_m_rows_ok(M))
         return small_m_config();
     if ((route == fp8bs::kRouteMX || route == fp8bs::kRoutePT) && N % 128 != 0)
         return cfg(7, 64);
@@ -143,7 +145,10 @@ fp8bs_config select(int route, int M, int N, int K)
     // 7168 39.7 against 55.3 us)
     if (M <= 128)
         return N % 256 == 0 && tiles(128, 256) >= kCUs ? cfg(14, 256) : cfg(0, 128);
-    if (N % 256 == 0 && tiles(256, 256) >= 2 * kCUs)
+    // 256 x 256 tiles from two rounds of the CUs; route MX from one (65536 x 1536 weights,
+    // M = 256: 28.3 against 32.0 us with 256 x 128 tiles; route BS, 24576 x 1536, M = 1024:
+    // 51.4 against 42.5)
+    if (N % 256 == 0 && tiles(256, 256) >= (route == fp8bs::kRouteMX ? 1 : 2) * kCUs)
         return cfg(2, 256);
     // the 256x128 / 128x256 tiles run warp-specialised (four loader waves beside the eight
     // math waves): measured 5-7% faster than the same tiles with every wave loading on the
@@ -185,11 +190,11 @@ int run(int route, const void* A, const void* a_scale, const void* B_prep, const
 {
     fp8bs::GemmArgs args{A, a_scale, B_prep, b_scale, C, M, N, K, stream};
     if (cfg && cfg->small_m >= fp8bs::kDecodeAuto && cfg->small_m <= fp8bs::kDecodeLds) {
-        // the small-M kernel reads the activation scales of route MX row-major, so the packed
-        // route-MX entry points cannot use it (fp8mx_gemm_small_m does)
-        if (route == fp8bs::kRouteMX || !small_m_rows_ok(M))
+        // the route-MX entry points that come here carry the packed activation scales
+        if (!small_m_rows_ok(M))
             return FP8BS_E_CONFIG;
-        return hip_status(fp8bs::launch_decode(route, args, cfg->small_m));
+        const int r = route == fp8bs::kRouteMX ? fp8bs::kRouteMXPacked : route;
+        return hip_status(fp8bs::launch_decode(r, args, cfg->small_m));
     }
     fp8bs::GemmConfig gc;
     int st = check_config(route, cfg, N, &gc);

@@ -23,8 +23,9 @@
 //    only the wave's own vmcnt is waited for.
 // Routes:
 //  * BS: unscaled instruction + promote acc += p * (a_s[kb, m] * b_s[n/128, kb]);
-//  * MX: scaled instruction, activation exponents read row-major from a_e8m0 [M, K/32], weight
-//    exponents from the packed buffer of fp8mx_prep_weights;
+//  * MX: scaled instruction, activation exponents read row-major from a_e8m0 [M, K/32] (or,
+//    kRouteMXPacked, as the packed dwords of fp8mx_pack_a_scale, the sub-tile picked by op_sel),
+//    weight exponents from the packed buffer of fp8mx_prep_weights;
 //  * PT: in-place accumulation, a_s[m] * b_s[n] applied once at the end.
 #include "device.hpp"
 #include "launch.hpp"
@@ -34,6 +35,29 @@ namespace fp8bs {
 namespace {
 
 constexpr int kDecodeWaves = 8;
+
+constexpr bool is_mx(int route) { return route == kRouteMX || route == kRouteMXPacked; }
+
+// Scaled instruction with the activation exponent taken from byte `sel` of a packed dword (the
+// byte select must be a compile-time constant; sel is one after unrolling).
+template <int SEL>
+__device__ __forceinline__ v4f mfma_packed_sel(const v8i& b, const v8i& a, const v4f& c, int sb, int sa_dword)
+{
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, kFmtE4M3, kFmtE4M3, 0, sb, SEL, sa_dword);
+}
+__device__ __forceinline__ v4f mfma_packed(int sel, const v8i& b, const v8i& a, const v4f& c, int sb, int sa_dword)
+{
+    switch (sel & 3) {
+    case 0:
+        return mfma_packed_sel<0>(b, a, c, sb, sa_dword);
+    case 1:
+        return mfma_packed_sel<1>(b, a, c, sb, sa_dword);
+    case 2:
+        return mfma_packed_sel<2>(b, a, c, sb, sa_dword);
+    default:
+        return mfma_packed_sel<3>(b, a, c, sb, sa_dword);
+    }
+}
 
 // Lane l = i + 16q reads bytes [16q, 16q+16) and [64+16q, 64+16q+16) of the 128-byte K block of
 // row `row` (the fragment layout of the 16x16x128 instruction).
@@ -92,12 +116,20 @@ decode_direct_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_s
             const uint32_t wd = ((const uint32_t*)b_scale)[((size_t)kb * (N >> 6) + (jt >> 2)) * 64 + lane];
             const int sbyte = (int)((wd >> (8 * (jt & 3))) & 0xffu);
             const int G = K >> 5;
+            // packed activation exponents: dword (kb * M/64 + chunk) * 64 + lane, byte = sub-tile
+            uint32_t ad = 0;
+            if constexpr (ROUTE == kRouteMXPacked)
+                ad = ((const uint32_t*)a_scale)[((size_t)kb * (M >> 6) + blockIdx.y) * 64 + lane];
 #pragma unroll
             for (int si = 0; si < SI; ++si) {
                 const v8i af = load_frag(A, arow[si], K, kb, q);
-                const int sabyte = ((const uint8_t*)a_scale)[(size_t)arow[si] * G + 4 * kb + q];
-                acc[si] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af, acc[si], kFmtE4M3, kFmtE4M3, 0,
-                                                                          sbyte, 0, sabyte);
+                if constexpr (ROUTE == kRouteMXPacked) {
+                    acc[si] = mfma_packed(si, bf, af, acc[si], sbyte, (int)ad);
+                } else {
+                    const int sabyte = ((const uint8_t*)a_scale)[(size_t)arow[si] * G + 4 * kb + q];
+                    acc[si] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, af, acc[si], kFmtE4M3, kFmtE4M3,
+                                                                              0, sbyte, 0, sabyte);
+                }
             }
         }
     }
@@ -167,7 +199,7 @@ template <int ROUTE, int SI>
 struct DBuf {
     static constexpr int kA = 16 * SI * 128;
     static constexpr int kB = 16 * 128;
-    static constexpr int kS = ROUTE == kRoutePT ? 0 : 512;
+    static constexpr int kS = ROUTE == kRoutePT ? 0 : 512;  // a_s / a_e8m0 in [0, 256), b_s in [256, 512)
     static constexpr int kBytes = kA + kB + kS;
     static constexpr int kLoads = 2 * SI + 2 + (ROUTE == kRoutePT ? 0 : 2);
 };
@@ -220,6 +252,9 @@ decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scal
     } else if constexpr (ROUTE == kRouteMX) {
         voffSA = min(m0 + lane, M - 1) * (K >> 5);
         voffSB = ((jt >> 2) * 64 + lane) * 4;
+    } else if constexpr (ROUTE == kRouteMXPacked) {  // packed dword (kb*M/64 + chunk)*64 + lane
+        voffSA = ((int)blockIdx.y * 64 + lane) * 4;
+        voffSB = ((jt >> 2) * 64 + lane) * 4;
     }
 
     auto issue = [&](int kb, int b) {
@@ -235,8 +270,9 @@ decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scal
         if constexpr (ROUTE == kRouteBS) {
             dma<4>(rsSA, sb + D::kA + D::kB, voffSA, __builtin_amdgcn_readfirstlane(kb * M * 4));
             dma<4>(rsSB, sb + D::kA + D::kB + 256, voffSB, __builtin_amdgcn_readfirstlane(kb * 4));
-        } else if constexpr (ROUTE == kRouteMX) {
-            dma<4>(rsSA, sb + D::kA + D::kB, voffSA, __builtin_amdgcn_readfirstlane(kb * 4));
+        } else if constexpr (is_mx(ROUTE)) {
+            const int soff_a = ROUTE == kRouteMX ? kb * 4 : kb * (M >> 6) * 256;
+            dma<4>(rsSA, sb + D::kA + D::kB, voffSA, __builtin_amdgcn_readfirstlane(soff_a));
             dma<4>(rsSB, sb + D::kA + D::kB + 256, voffSB, __builtin_amdgcn_readfirstlane(kb * (N >> 6) * 256));
         }
     };
@@ -282,12 +318,17 @@ decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scal
         } else {
             const uint32_t wd = ((const uint32_t*)(base + D::kA + D::kB + 256))[lane];
             const int sbyte = (int)((wd >> (8 * (jt & 3))) & 0xffu);
+            const uint32_t apk = ((const uint32_t*)(base + D::kA + D::kB))[lane];  // packed: this lane's dword
 #pragma unroll
             for (int si = 0; si < SI; ++si) {
-                const uint32_t ad = ((const uint32_t*)(base + D::kA + D::kB))[16 * si + i];
-                const int sabyte = (int)((ad >> (8 * q)) & 0xffu);
-                acc[si] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bf, frag(base + si * 16 * 128), acc[si],
-                                                                          kFmtE4M3, kFmtE4M3, 0, sbyte, 0, sabyte);
+                if constexpr (ROUTE == kRouteMXPacked) {
+                    acc[si] = mfma_packed(si, bf, frag(base + si * 16 * 128), acc[si], sbyte, (int)apk);
+                } else {
+                    const uint32_t ad = ((const uint32_t*)(base + D::kA + D::kB))[16 * si + i];
+                    const int sabyte = (int)((ad >> (8 * q)) & 0xffu);
+                    acc[si] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        bf, frag(base + si * 16 * 128), acc[si], kFmtE4M3, kFmtE4M3, 0, sbyte, 0, sabyte);
+                }
             }
         }
         // every read of this buffer is done before the next iteration's loads refill it
@@ -376,6 +417,8 @@ hipError_t launch_decode(int route, const GemmArgs& a, int variant)
         return launch_route<kRouteBS>(si, variant, a);
     if (route == kRoutePT)
         return launch_route<kRoutePT>(si, variant, a);
+    if (route == kRouteMXPacked)
+        return launch_route<kRouteMXPacked>(si, variant, a);
     return launch_route<kRouteMX>(si, variant, a);
 }
 

@@ -7,6 +7,9 @@
 namespace fp8bs {
 
 enum { kRouteBS = 0, kRouteMX = 1, kRoutePT = 2 };
+// Small-M kernel only: route MX with the packed activation scales of fp8mx_pack_a_scale (M % 64
+// == 0) instead of the row-major a_e8m0 bytes.
+constexpr int kRouteMXPacked = 3;
 
 struct GemmArgs {
     const void* A;        // [M, K] e4m3
@@ -41,7 +44,8 @@ hipError_t launch_pack_scales(const void* e8m0, void* packed, int rows, int K, i
 // Small-M kernel (decode.hip): M >= 1 in chunks of kDecodeMaxRows rows (at most kDecodeMaxChunks
 // chunks: the grid's y extent), N % 64 == 0, K % 128 == 0. Route BS
 // takes a_scale [K/128, M] fp32 as the main kernel does; route MX takes the activation
-// exponents row-major, a_e8m0 [M, K/32]; route PT a_scale [M], b_scale [N]. Variant: kDecodeAuto
+// exponents row-major, a_e8m0 [M, K/32] (kRouteMXPacked: packed as for the main kernel);
+// route PT a_scale [M], b_scale [N]. Variant: kDecodeAuto
 // (chosen by shape), kDecodeDirect (fragments loaded straight into registers) or kDecodeLds
 // (operands staged through LDS by direct-to-LDS loads); all three give identical results.
 constexpr int kDecodeMaxRows = 64;

@@ -199,8 +199,9 @@ typedef struct {
                       * four extra waves issue every global -> LDS load, the others compute    */
     int small_m;     /* non-zero: the small-M kernel (every other field is ignored): one        *
                       * workgroup per 16 output columns and 64-row chunk of A streams the      *
-                      * weights, its waves split K (routes BS and PT, M <= 64 * 65535; route   *
-                      * MX through fp8mx_gemm_small_m).                                        *
+                      * weights, its waves split K (M <= 64 * 65535; route MX with the packed  *
+                      * activation scales of its main entry, or fp8mx_gemm_small_m for         *
+                      * row-major ones).                                                       *
                       * 1: variant chosen by shape; 2: fragments loaded straight into          *
                       * registers; 3: operands staged through LDS. Same results for all three; *
                       * other values are rejected with FP8BS_E_CONFIG                          */

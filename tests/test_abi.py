@@ -112,8 +112,9 @@ def test_select_config_is_shape_driven(fb):
                                 (fb.ROUTE_BS, (65, 128, 7168), 1), (fb.ROUTE_PT, (33, 4096, 512), 1),
                                 (fb.ROUTE_BS, (512, 2048, 7168), 1), (fb.ROUTE_PT, (96, 1536, 7168), 1),
                                 (fb.ROUTE_BS, (640, 2048, 7168), 0), (fb.ROUTE_BS, (192, 7168, 7168), 0),
-                                (fb.ROUTE_BS, (96, 7168, 768), 0), (fb.ROUTE_MX, (128, 2048, 7168), 0),
-                                (fb.ROUTE_PT, (0, 4096, 512), 0), (fb.ROUTE_MX, (64, 4096, 512), 0)):
+                                (fb.ROUTE_BS, (96, 7168, 768), 0), (fb.ROUTE_MX, (128, 2048, 7168), 1),
+                                (fb.ROUTE_MX, (128, 7168, 7168), 0), (fb.ROUTE_MX, (64, 32768, 1536), 0),
+                                (fb.ROUTE_PT, (0, 4096, 512), 0), (fb.ROUTE_MX, (64, 4096, 512), 1)):
         c = fb.fp8bs_select_config(route, *shape)
         assert c.small_m == small, (route, shape)
         if small:
@@ -130,6 +131,9 @@ def test_select_config_is_shape_driven(fb):
         assert (c.block_m, c.block_n, c.pingpong) == (128, 128, 0), (route, shape)
     c = fb.fp8bs_select_config(fb.ROUTE_BS, 129, 65536, 1536)
     assert c.block_m == 256
+    # 256x256 tiles from one round of the CUs for route MX, from two for the others
+    assert (fb.fp8bs_select_config(fb.ROUTE_MX, 256, 65536, 1536).block_m,
+            fb.fp8bs_select_config(fb.ROUTE_BS, 1024, 24576, 1536).block_n) == (256, 128)
     # 128x128 tiles only while they need no more rounds of the CUs than 256x128 tiles
     for shape, tile in (((640, 7168, 7168), (256, 128)), ((1024, 7168, 7168), (256, 128)),
                         ((1024, 2048, 7168), (128, 128)), ((200, 4096, 512), (128, 128))):

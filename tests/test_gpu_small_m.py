@@ -86,6 +86,28 @@ def test_small_m_mx(fb, oracle, M, N, K):
     parity(bits(C), ref, f"small-M mx {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("variant", [AUTO, DIRECT, LDS])
+@pytest.mark.parametrize("M,N,K", [(64, 256, 512), (128, 384, 1024), (192, 512, 2048), (64, 4096, 384),
+                                   (320, 192, 1280)])
+def test_small_m_mx_packed_scales(fb, oracle, M, N, K, variant):
+    """Route MX through the main entry's packed activation scales (fp8mx_gemm_with_config with
+    a small-M configuration): parity with the oracle, and bitwise equal to the row-major entry
+    fp8mx_gemm_small_m (the same exponents reach the same instructions)."""
+    y = workload.mx_inputs(M, N, K, M + 5 * N + K)
+    Bp, pb = fb.mx_prep_weights(to_dev(y.B), to_dev(y.b_e8m0))
+    A = to_dev(y.A)
+    C = torch.full((M, N), 3.0, dtype=torch.bfloat16, device=dev())
+    fb.fp8mx_gemm_with_config(A, fb.mx_pack_a_scale(to_dev(y.a_e8m0)), Bp, pb, C, _small(fb, variant))
+    C2 = torch.full((M, N), 5.0, dtype=torch.bfloat16, device=dev())
+    fb.fp8mx_gemm_small_m(A, to_dev(y.a_e8m0), Bp, pb, C2)
+    torch.cuda.synchronize()
+    _, ref = oracle.mx_gemm(y.A, y.a_e8m0, y.B, y.b_e8m0)
+    got = bits(C)
+    parity(got, ref, f"small-M mx packed {M}x{N}x{K} variant {variant}")
+    if variant == AUTO:
+        assert np.array_equal(got, bits(C2))
+
+
 @pytest.mark.parametrize("variant", [DIRECT, LDS])
 @pytest.mark.parametrize("M,K", [(7, 512), (48, 1280), (64, 3072)])
 def test_small_m_integer_exact(fb, oracle, M, K, variant):
@@ -125,7 +147,8 @@ def test_plain_entry_picks_small_m(fb, oracle):
     assert fb.fp8bs_select_config(fb.ROUTE_BS, 65, 2048, 7168).small_m == 1  # 64-row chunks
     assert fb.fp8bs_select_config(fb.ROUTE_BS, 1024, 2048, 7168).small_m == 0
     assert fb.fp8bs_select_config(fb.ROUTE_PT, 1, 4096, 512).small_m == 1
-    assert fb.fp8bs_select_config(fb.ROUTE_MX, 64, 4096, 512).small_m == 0
+    assert fb.fp8bs_select_config(fb.ROUTE_MX, 64, 4096, 512).small_m == 1  # packed activation scales
+    assert fb.fp8bs_select_config(fb.ROUTE_MX, 64, 32768, 1536).small_m == 0
     x = workload.bs_inputs(24, 2048, 1024, 2)
     got = run_bs(fb, x)  # plain entry point
     assert np.array_equal(got, _run_bs_cfg(fb, x, _small(fb)))

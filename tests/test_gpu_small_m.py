@@ -154,6 +154,32 @@ def test_plain_entry_picks_small_m(fb, oracle):
     assert np.array_equal(got, _run_bs_cfg(fb, x, _small(fb)))
 
 
+@pytest.mark.parametrize("route,M,N,K", [("bs", 200, 2048, 4096), ("pt", 130, 1536, 4608), ("mx", 128, 2048, 4096),
+                                         ("mx", 64, 512, 1280)])
+def test_plain_entry_small_m_routes(fb, oracle, route, M, N, K):
+    """Shapes on which the plain entry points select the small-M kernel (64-row chunks over deep
+    K; route MX on its packed activation scales): full-C parity with the oracle."""
+    rid = {"bs": fb.ROUTE_BS, "pt": fb.ROUTE_PT, "mx": fb.ROUTE_MX}[route]
+    assert fb.fp8bs_select_config(rid, M, N, K).small_m == 1, (route, M, N, K)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev())
+    if route == "bs":
+        x = workload.bs_inputs(M, N, K, M + N)
+        got = run_bs(fb, x, C)
+        _, ref = oracle.bs_gemm(x.A, x.a_scale, x.B, x.b_scale)
+    elif route == "pt":
+        z = workload.pt_inputs(M, N, K, M + N)
+        got = run_pt(fb, z)
+        _, ref = oracle.pt_gemm(z.A, z.a_scale, z.B, z.b_scale)
+    else:
+        y = workload.mx_inputs(M, N, K, M + N)
+        Bp, pb = fb.mx_prep_weights(to_dev(y.B), to_dev(y.b_e8m0))
+        fb.fp8mx_gemm(to_dev(y.A), fb.mx_pack_a_scale(to_dev(y.a_e8m0)), Bp, pb, C)
+        torch.cuda.synchronize()
+        got = bits(C)
+        _, ref = oracle.mx_gemm(y.A, y.a_e8m0, y.B, y.b_e8m0)
+    parity(got, ref, f"plain {route} {M}x{N}x{K}")
+
+
 def test_small_m_rejects(fb):
     y = workload.bs_inputs(8, 256, 256, 0)
     for variant in (-1, 4):  # no such variant

@@ -189,9 +189,10 @@ int run(int route, const void* A, const void* a_scale, const void* B_prep, const
         int M, int N, int K, const fp8bs_config* cfg, hipStream_t stream)
 {
     fp8bs::GemmArgs args{A, a_scale, B_prep, b_scale, C, M, N, K, stream};
-    if (cfg && cfg->small_m >= fp8bs::kDecodeAuto && cfg->small_m <= fp8bs::kDecodeLds) {
+    if (cfg && cfg->small_m >= fp8bs::kDecodeAuto && cfg->small_m <= fp8bs::kDecodeLdsPair) {
         // the route-MX entry points that come here carry the packed activation scales
-        if (!small_m_rows_ok(M))
+        if (!small_m_rows_ok(M) ||
+            (cfg->small_m == fp8bs::kDecodeLdsPair && (std::min(M, fp8bs::kDecodeMaxRows) > 32 || N % 32 != 0)))
             return FP8BS_E_CONFIG;
         const int r = route == fp8bs::kRouteMX ? fp8bs::kRouteMXPacked : route;
         return hip_status(fp8bs::launch_decode(r, args, cfg->small_m));

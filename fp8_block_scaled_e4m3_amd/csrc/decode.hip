@@ -194,33 +194,36 @@ __device__ __forceinline__ void wait_vm()
 
 __device__ __forceinline__ uint32_t swz(uint32_t row) { return (row >> 1) & 7u; }
 
-// Per-wave LDS buffer of one K block: [A: 16*SI rows x 128 B][B: 16 rows x 128 B][scales 512 B]
-template <int ROUTE, int SI>
+// Per-wave LDS buffer of one K block: [A: 16*SI rows x 128 B][B: 16*JT rows x 128 B][scales
+// 512 B]; JT = 16-row weight sub-tiles per workgroup
+template <int ROUTE, int SI, int JT>
 struct DBuf {
     static constexpr int kA = 16 * SI * 128;
-    static constexpr int kB = 16 * 128;
+    static constexpr int kB = 16 * JT * 128;
     static constexpr int kS = ROUTE == kRoutePT ? 0 : 512;  // a_s / a_e8m0 in [0, 256), b_s in [256, 512)
     static constexpr int kBytes = kA + kB + kS;
-    static constexpr int kLoads = 2 * SI + 2 + (ROUTE == kRoutePT ? 0 : 2);
+    static constexpr int kLoads = 2 * SI + 2 * JT + (ROUTE == kRoutePT ? 0 : 2);
 };
 
-template <int SI>
-constexpr int waves_for() { return SI == 4 ? 7 : kDecodeWaves; }  // LDS: two buffers per wave
+// LDS: two buffers per wave
+template <int SI, int JT>
+constexpr int waves_for() { return SI == 4 ? 7 : kDecodeWaves; }
 
-template <int ROUTE, int SI>
-__global__ void __launch_bounds__(waves_for<SI>() * 64)
+template <int ROUTE, int SI, int JT>
+__global__ void __launch_bounds__((waves_for<SI, JT>() * 64))
 decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale, const uint8_t* __restrict__ B,
               const void* __restrict__ b_scale, uint16_t* __restrict__ C, int M, int N, int K)
 {
-    using D = DBuf<ROUTE, SI>;
-    constexpr int NW = waves_for<SI>();
+    static_assert(JT == 1 || (JT == 2 && SI <= 2), "two weight sub-tiles per workgroup up to 32 rows");
+    using D = DBuf<ROUTE, SI, JT>;
+    constexpr int NW = waves_for<SI, JT>();
     static_assert(2 * NW * D::kBytes <= 160 * 1024, "LDS");
-    static_assert(NW * SI * 64 * 16 <= 2 * NW * D::kBytes, "reduction fits the operand buffers");
+    static_assert(NW * SI * JT * 64 * 16 <= 2 * NW * D::kBytes, "reduction fits the operand buffers");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NW * D::kBytes];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int i = lane & 15, q = lane >> 4;
-    const int jt = blockIdx.x;
+    const int jt = blockIdx.x * JT;  // first 16-row sub-tile of the prepared weights
     const int m0 = blockIdx.y * kDecodeMaxRows;  // first activation row of the chunk
     const int KB = K >> 7;
     const int kb0 = (wave * KB) / NW, kb1 = ((wave + 1) * KB) / NW;
@@ -228,7 +231,7 @@ decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scal
     uint8_t* mybuf = lds + wave * 2 * D::kBytes;
 
     // DMA lane offsets (without the K block term): A group g covers rows m0+8g .. m0+8g+7
-    // (clamped to M-1), B group g rows 8g..8g+7 of the sub-tile; lane l -> row l/8, physical
+    // (clamped to M-1), B group g rows 8g..8g+7 of the sub-tiles; lane l -> row l/8, physical
     // chunk l%8 holding logical chunk (l%8) ^ swz(row)
     const int r8 = lane >> 3, c8 = lane & 7;
     int voffA[2 * SI];
@@ -237,9 +240,9 @@ decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scal
         const int row = 8 * g + r8;
         voffA[g] = min(m0 + row, M - 1) * K + ((c8 ^ (int)swz(row)) << 4);
     }
-    int voffB[2];
+    int voffB[2 * JT];
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < 2 * JT; ++g) {
         const int row = 8 * g + r8;
         voffB[g] = (jt * 16 + row) * K + ((c8 ^ (int)swz(row)) << 4);
     }
@@ -265,7 +268,7 @@ decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scal
         for (int g = 0; g < 2 * SI; ++g)
             dma<16>(rsA, sb + g * 1024, voffA[g], koff);
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
+        for (int g = 0; g < 2 * JT; ++g)
             dma<16>(rsB, sb + D::kA + g * 1024, voffB[g], koff);
         if constexpr (ROUTE == kRouteBS) {
             dma<4>(rsSA, sb + D::kA + D::kB, voffSA, __builtin_amdgcn_readfirstlane(kb * M * 4));
@@ -284,10 +287,12 @@ decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scal
         return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     };
 
-    v4f acc[SI];
+    v4f acc[JT][SI];
 #pragma unroll
-    for (int si = 0; si < SI; ++si)
-        acc[si] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < JT; ++t)
+#pragma unroll
+        for (int si = 0; si < SI; ++si)
+            acc[t][si] = v4f{0.f, 0.f, 0.f, 0.f};
 
     if (kb0 < kb1)
         issue(kb0, 0);
@@ -301,33 +306,40 @@ decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scal
         }
         asm volatile("" ::: "memory");  // the buffer's reads stay below the wait
         const uint8_t* base = mybuf + b * D::kBytes;
-        const v8i bf = frag(base + D::kA);
-        if constexpr (ROUTE == kRouteBS) {
-            const float sb = *(const float*)(base + D::kA + D::kB + 256);
+        v8i af[SI];
 #pragma unroll
-            for (int si = 0; si < SI; ++si) {
-                const v8i af = frag(base + si * 16 * 128);
-                const float sa = ((const float*)(base + D::kA + D::kB))[16 * si + i];  // row m0+16si+i, clamped
-                const v4f p = mfma_f8(bf, af, v4f{0.f, 0.f, 0.f, 0.f});
-                acc[si] += p * (sa * sb);
-            }
-        } else if constexpr (ROUTE == kRoutePT) {
+        for (int si = 0; si < SI; ++si)
+            af[si] = frag(base + si * 16 * 128);
+        // the JT sub-tiles share their 128-row weight-scale block and 64-row exponent window
 #pragma unroll
-            for (int si = 0; si < SI; ++si)
-                acc[si] = mfma_f8(bf, frag(base + si * 16 * 128), acc[si]);
-        } else {
-            const uint32_t wd = ((const uint32_t*)(base + D::kA + D::kB + 256))[lane];
-            const int sbyte = (int)((wd >> (8 * (jt & 3))) & 0xffu);
-            const uint32_t apk = ((const uint32_t*)(base + D::kA + D::kB))[lane];  // packed: this lane's dword
+        for (int t = 0; t < JT; ++t) {
+            const v8i bf = frag(base + D::kA + t * 16 * 128);
+            if constexpr (ROUTE == kRouteBS) {
+                const float sb = *(const float*)(base + D::kA + D::kB + 256);
 #pragma unroll
-            for (int si = 0; si < SI; ++si) {
-                if constexpr (ROUTE == kRouteMXPacked) {
-                    acc[si] = mfma_packed(si, bf, frag(base + si * 16 * 128), acc[si], sbyte, (int)apk);
-                } else {
-                    const uint32_t ad = ((const uint32_t*)(base + D::kA + D::kB))[16 * si + i];
-                    const int sabyte = (int)((ad >> (8 * q)) & 0xffu);
-                    acc[si] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                        bf, frag(base + si * 16 * 128), acc[si], kFmtE4M3, kFmtE4M3, 0, sbyte, 0, sabyte);
+                for (int si = 0; si < SI; ++si) {
+                    const float sa = ((const float*)(base + D::kA + D::kB))[16 * si + i];  // row m0+16si+i, clamped
+                    const v4f p = mfma_f8(bf, af[si], v4f{0.f, 0.f, 0.f, 0.f});
+                    acc[t][si] += p * (sa * sb);
+                }
+            } else if constexpr (ROUTE == kRoutePT) {
+#pragma unroll
+                for (int si = 0; si < SI; ++si)
+                    acc[t][si] = mfma_f8(bf, af[si], acc[t][si]);
+            } else {
+                const uint32_t wd = ((const uint32_t*)(base + D::kA + D::kB + 256))[lane];
+                const int sbyte = (int)((wd >> (8 * ((jt + t) & 3))) & 0xffu);
+                const uint32_t apk = ((const uint32_t*)(base + D::kA + D::kB))[lane];  // packed: this lane's dword
+#pragma unroll
+                for (int si = 0; si < SI; ++si) {
+                    if constexpr (ROUTE == kRouteMXPacked) {
+                        acc[t][si] = mfma_packed(si, bf, af[si], acc[t][si], sbyte, (int)apk);
+                    } else {
+                        const uint32_t ad = ((const uint32_t*)(base + D::kA + D::kB))[16 * si + i];
+                        const int sabyte = (int)((ad >> (8 * q)) & 0xffu);
+                        acc[t][si] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            bf, af[si], acc[t][si], kFmtE4M3, kFmtE4M3, 0, sbyte, 0, sabyte);
+                    }
                 }
             }
         }
@@ -336,29 +348,45 @@ decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scal
     }
 
     __syncthreads();  // reduction storage reuses the operand buffers
-    v4f* red = (v4f*)lds;  // [wave][si][64]
+    v4f* red = (v4f*)lds;  // [wave][t][si][64]
 #pragma unroll
-    for (int si = 0; si < SI; ++si)
-        red[(wave * SI + si) * 64 + lane] = acc[si];
+    for (int t = 0; t < JT; ++t)
+#pragma unroll
+        for (int si = 0; si < SI; ++si)
+            red[((wave * JT + t) * SI + si) * 64 + lane] = acc[t][si];
     __syncthreads();
     if (wave < SI) {
+        // sub-tiles jt and jt+1 (jt even) hold output columns n..n+3 and n+4..n+7
         const int si = wave;
-        v4f s = red[si * 64 + lane];
-#pragma unroll
-        for (int w = 1; w < NW; ++w)
-            s += red[(w * SI + si) * 64 + lane];
         const int m = m0 + 16 * si + i;
         const int n = 64 * (jt >> 2) + 32 * ((jt & 3) >> 1) + 8 * q + 4 * (jt & 1);
-        if constexpr (ROUTE == kRoutePT) {
-            const float sa = ((const float*)a_scale)[min(m, M - 1)];
-            const v4f sbv = *(const v4f*)((const float*)b_scale + n);
-            s = s * (sbv * sa);
+        v4f s[JT];
+#pragma unroll
+        for (int t = 0; t < JT; ++t) {
+            s[t] = red[(t * SI + si) * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < NW; ++w)
+                s[t] += red[((w * JT + t) * SI + si) * 64 + lane];
+            if constexpr (ROUTE == kRoutePT) {
+                const float sa = ((const float*)a_scale)[min(m, M - 1)];
+                const v4f sbv = *(const v4f*)((const float*)b_scale + n + 4 * t);
+                s[t] = s[t] * (sbv * sa);
+            }
         }
         if (m < M) {
-            v2i packed;
-            packed.x = (int)pack_bf16x2(s.x, s.y);
-            packed.y = (int)pack_bf16x2(s.z, s.w);
-            *(v2i*)(C + (size_t)m * N + n) = packed;
+            if constexpr (JT == 2) {
+                v4i packed;
+                packed.x = (int)pack_bf16x2(s[0].x, s[0].y);
+                packed.y = (int)pack_bf16x2(s[0].z, s[0].w);
+                packed.z = (int)pack_bf16x2(s[1].x, s[1].y);
+                packed.w = (int)pack_bf16x2(s[1].z, s[1].w);
+                *(v4i*)(C + (size_t)m * N + n) = packed;
+            } else {
+                v2i packed;
+                packed.x = (int)pack_bf16x2(s[0].x, s[0].y);
+                packed.y = (int)pack_bf16x2(s[0].z, s[0].w);
+                *(v2i*)(C + (size_t)m * N + n) = packed;
+            }
         }
     }
 }
@@ -370,9 +398,14 @@ void launch_one(int variant, const GemmArgs& a)
     const uint8_t* A = (const uint8_t*)a.A;
     const uint8_t* B = (const uint8_t*)a.B;
     uint16_t* C = (uint16_t*)a.C;
-    if (variant == kDecodeLds)
-        hipLaunchKernelGGL((decode_lds_kernel<ROUTE, SI>), dim3(a.N / 16, chunks), dim3(waves_for<SI>() * 64), 0, a.stream,
-                           A, a.a_scale, B, a.b_scale, C, a.M, a.N, a.K);
+    if (variant == kDecodeLdsPair) {
+        if constexpr (SI <= 2)
+            hipLaunchKernelGGL((decode_lds_kernel<ROUTE, SI, 2>), dim3(a.N / 32, chunks),
+                               dim3(waves_for<SI, 2>() * 64), 0, a.stream, A, a.a_scale, B, a.b_scale, C, a.M, a.N,
+                               a.K);
+    } else if (variant == kDecodeLds)
+        hipLaunchKernelGGL((decode_lds_kernel<ROUTE, SI, 1>), dim3(a.N / 16, chunks), dim3(waves_for<SI, 1>() * 64),
+                           0, a.stream, A, a.a_scale, B, a.b_scale, C, a.M, a.N, a.K);
     else
         hipLaunchKernelGGL((decode_direct_kernel<ROUTE, SI>), dim3(a.N / 16, chunks), dim3(kDecodeWaves * 64), 0, a.stream,
                            A, a.a_scale, B, a.b_scale, C, a.M, a.N, a.K);
@@ -405,12 +438,24 @@ hipError_t launch_decode(int route, const GemmArgs& a, int variant)
     if (a.M <= 0 || (a.M + kDecodeMaxRows - 1) / kDecodeMaxRows > kDecodeMaxChunks || a.N % 64 != 0 ||
         a.K % 128 != 0)
         return hipErrorInvalidValue;
+    if (variant == kDecodeLdsPair && (min(a.M, kDecodeMaxRows) > 32 || a.N % 32 != 0))
+        return hipErrorInvalidValue;
     if (variant == kDecodeAuto) {
         // the LDS-staged variant unless the activations are few and every wave owns at most two
         // K blocks (there the extra LDS round trip is not repaid: 1 x 65536 x 1536 direct 16.3
         // us, staged 18.1; 64 x 2048 x 7168 direct 17.8, staged 7.3)
         const int blocks_per_wave = ((a.K >> 7) + kDecodeWaves - 1) / kDecodeWaves;
         variant = (a.M > 4 || blocks_per_wave >= 3) ? kDecodeLds : kDecodeDirect;
+        // 17 to 32 rows: two weight sub-tiles per workgroup halve the activation re-reads (7168 x
+        // 7168 weights, M = 32: 10.0 against 11.8 us; 16384 x 4096: 13.3 against 16.1), while
+        // the grid keeps 192 workgroups (4096 x 4096: 5.2 against 4.6; 2048 x 7168: 6.1 against
+        // 5.1) and K <= 7168 (28672 x 8192, already near HBM speed: 50.3 against 43.0); with at
+        // most 16 rows they lose
+        const int rows = min(a.M, kDecodeMaxRows);
+        const int chunks = (a.M + kDecodeMaxRows - 1) / kDecodeMaxRows;
+        if (variant == kDecodeLds && rows > 16 && rows <= 32 && a.N % 32 == 0 && (a.N / 32) * chunks >= 192 &&
+            a.K <= 7168)
+            variant = kDecodeLdsPair;
     }
     const int si = (min(a.M, kDecodeMaxRows) + 15) / 16;
     if (route == kRouteBS)

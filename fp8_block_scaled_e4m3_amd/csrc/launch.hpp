@@ -45,12 +45,13 @@ hipError_t launch_pack_scales(const void* e8m0, void* packed, int rows, int K, i
 // chunks: the grid's y extent), N % 64 == 0, K % 128 == 0. Route BS
 // takes a_scale [K/128, M] fp32 as the main kernel does; route MX takes the activation
 // exponents row-major, a_e8m0 [M, K/32] (kRouteMXPacked: packed as for the main kernel);
-// route PT a_scale [M], b_scale [N]. Variant: kDecodeAuto
-// (chosen by shape), kDecodeDirect (fragments loaded straight into registers) or kDecodeLds
-// (operands staged through LDS by direct-to-LDS loads); all three give identical results.
+// route PT a_scale [M], b_scale [N]. Variant: kDecodeAuto (chosen by shape), kDecodeDirect
+// (fragments loaded straight into registers), kDecodeLds (operands staged through LDS by
+// direct-to-LDS loads) or kDecodeLdsPair (the same with two 16-row weight sub-tiles per
+// workgroup; min(M, 64) <= 32 and N % 32 == 0); results agree bit for bit up to 48 rows.
 constexpr int kDecodeMaxRows = 64;
 constexpr int kDecodeMaxChunks = 65535;
-constexpr int kDecodeAuto = 1, kDecodeDirect = 2, kDecodeLds = 3;
+constexpr int kDecodeAuto = 1, kDecodeDirect = 2, kDecodeLds = 3, kDecodeLdsPair = 4;
 hipError_t launch_decode(int route, const GemmArgs& a, int variant);
 
 // Activation quantiser of route kRouteBS (scales: fp32 [K/128, M]) or kRouteMX (scales: ue8m0

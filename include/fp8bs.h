@@ -203,8 +203,10 @@ typedef struct {
                       * activation scales of its main entry, or fp8mx_gemm_small_m for         *
                       * row-major ones).                                                       *
                       * 1: variant chosen by shape; 2: fragments loaded straight into          *
-                      * registers; 3: operands staged through LDS. Same results for all three; *
-                      * other values are rejected with FP8BS_E_CONFIG                          */
+                      * registers; 3: operands staged through LDS; 4: as 3 with two 16-row     *
+                      * weight sub-tiles per workgroup (at most 32 rows per launch chunk, N %  *
+                      * 32 == 0). Same results for all up to 48 rows; other values, or 4 where *
+                      * it does not apply, are rejected with FP8BS_E_CONFIG                    */
 } fp8bs_config;
 
 /* The configuration fp8bs_gemm (route FP8BS_ROUTE_BS), fp8mx_gemm (FP8BS_ROUTE_MX) or

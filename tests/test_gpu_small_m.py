@@ -21,7 +21,7 @@ def fb():
     return fb
 
 
-AUTO, DIRECT, LDS = 1, 2, 3
+AUTO, DIRECT, LDS, PAIR = 1, 2, 3, 4  # PAIR: LDS-staged, two weight sub-tiles per workgroup
 
 
 def _small(fb, variant=AUTO):
@@ -43,9 +43,15 @@ def _run_bs_cfg(fb, x, cfg):
     return bits(C)
 
 
-@pytest.mark.parametrize("variant", [DIRECT, LDS])
+def _applies(variant, M):
+    return variant != PAIR or M <= 32
+
+
+@pytest.mark.parametrize("variant", [DIRECT, LDS, PAIR])
 @pytest.mark.parametrize("M,N,K", [s for s in SHAPES if s[1] % 128 == 0])
 def test_small_m_bs(fb, oracle, M, N, K, variant):
+    if not _applies(variant, M):
+        pytest.skip("two sub-tiles per workgroup take at most 32 rows")
     x = workload.bs_inputs(M, N, K, M + N)
     got = _run_bs_cfg(fb, x, _small(fb, variant))
     _, ref = oracle.bs_gemm(x.A, x.a_scale, x.B, x.b_scale)
@@ -54,9 +60,11 @@ def test_small_m_bs(fb, oracle, M, N, K, variant):
     assert np.array_equal(got, again)  # deterministic: fixed-order sum of the wave partials
 
 
-@pytest.mark.parametrize("variant", [DIRECT, LDS])
+@pytest.mark.parametrize("variant", [DIRECT, LDS, PAIR])
 @pytest.mark.parametrize("M,N,K", SHAPES)
 def test_small_m_pt(fb, oracle, M, N, K, variant):
+    if not _applies(variant, M):
+        pytest.skip("two sub-tiles per workgroup take at most 32 rows")
     z = workload.pt_inputs(M, N, K, M * 7 + N)
     got = run_pt(fb, z, _small(fb, variant))
     _, ref = oracle.pt_gemm(z.A, z.a_scale, z.B, z.b_scale)
@@ -72,10 +80,13 @@ def test_small_m_variants_bitwise_equal(fb, M, N, K):
     direct = _run_bs_cfg(fb, x, _small(fb, DIRECT))
     staged = _run_bs_cfg(fb, x, _small(fb, LDS))
     assert np.array_equal(direct, staged), f"{int((direct != staged).sum())} differ"
+    if M <= 32:
+        pair = _run_bs_cfg(fb, x, _small(fb, PAIR))
+        assert np.array_equal(pair, staged), f"pair: {int((pair != staged).sum())} differ"
     assert np.array_equal(_run_bs_cfg(fb, x, _small(fb, AUTO)), direct)
 
 
-@pytest.mark.parametrize("M,N,K", [s for s in SHAPES if s[2] >= 256])
+@pytest.mark.parametrize("M,N,K", [s for s in SHAPES if s[2] >= 256] + [(24, 8192, 1024), (32, 8192, 4096)])
 def test_small_m_mx(fb, oracle, M, N, K):
     y = workload.mx_inputs(M, N, K, M + 3 * N)
     Bp, pb = fb.mx_prep_weights(to_dev(y.B), to_dev(y.b_e8m0))
@@ -108,9 +119,11 @@ def test_small_m_mx_packed_scales(fb, oracle, M, N, K, variant):
         assert np.array_equal(got, bits(C2))
 
 
-@pytest.mark.parametrize("variant", [DIRECT, LDS])
+@pytest.mark.parametrize("variant", [DIRECT, LDS, PAIR])
 @pytest.mark.parametrize("M,K", [(7, 512), (48, 1280), (64, 3072)])
 def test_small_m_integer_exact(fb, oracle, M, K, variant):
+    if not _applies(variant, M):
+        pytest.skip("two sub-tiles per workgroup take at most 32 rows")
     """Small-integer codes with power-of-two scales: every partial and the fixed-order sum of
     the wave partials are exact in fp32, so the output equals the oracle bit for bit."""
     N = 256
@@ -182,10 +195,14 @@ def test_plain_entry_small_m_routes(fb, oracle, route, M, N, K):
 
 def test_small_m_rejects(fb):
     y = workload.bs_inputs(8, 256, 256, 0)
-    for variant in (-1, 4):  # no such variant
+    for variant in (-1, 5):  # no such variant
         with pytest.raises(fb.Fp8bsError) as e:
             _run_bs_cfg(fb, y, _small(fb, variant))
         assert e.value.status == 4
+    z = workload.bs_inputs(33, 256, 256, 0)  # two sub-tiles per workgroup take at most 32 rows
+    with pytest.raises(fb.Fp8bsError) as e:
+        _run_bs_cfg(fb, z, _small(fb, PAIR))
+    assert e.value.status == 4
     d = dev()
     A = torch.zeros((65, 256), dtype=torch.uint8, device=d)
     buf = torch.zeros(1 << 16, dtype=torch.uint8, device=d)

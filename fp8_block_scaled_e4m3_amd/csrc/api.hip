@@ -113,38 +113,48 @@ fp8bs_config select(int route, int M, int N, int K)
         const int xcd = group_m * (N / block_n) <= 2 * kCUs ? 1 : 2;
         return make_config(variant, group_m, xcd, 1);
     };
-    // Small M (the decode regime): the small-M kernel streams the weights once at close to
-    // HBM bandwidth. It wins whenever the main kernel's one row of tiles would not fill the CUs
-    // (measured: 7168 x 7168 weights, M = 1: 9.1 vs 37.5 us, M = 64: 16.5 vs 37.6 us), and for
-    // M <= 4 everywhere; from M = 5 to 16 it loses where a row of 128 x 256 tiles already fills
-    // the CUs (65536 x 1536 weights, M = 8 and 16: 18.5 vs 17.5 us), above 16 rows wherever a
-    // row of 128 x 128 tiles does (M = 64: 65536 x 1536 43.8 vs 18.9 us, 32768 x 1536 22.3 vs
-    // 11.5 us, 32768 x 7168 61.6 vs 39.7 us). Route MX (M = 64 here) the same, the kernel then
-    // reading the packed activation scales (8192 x 1280 weights: 6.1 vs 8.1 us).
-    if (M >= 1 && M <= fp8bs::kDecodeMaxRows) {
-        const bool row_fills_128x256 = N % 256 == 0 && N / 256 >= kCUs;
-        const bool row_fills_128x128 = N / (N % 128 == 0 ? 128 : 64) >= kCUs;
-        if (M <= 4 || (M <= 16 ? !row_fills_128x256 : !row_fills_128x128))
+    // The small-M kernel against the main kernel. With few rows the main kernel runs one round
+    // of 128-row tiles whose time is set by the K loop (about 3.7 us + 0.6 us per K block), while
+    // the small-M kernel splits K over its waves and spreads the work over chunks x N/16
+    // workgroups: its time grows with W = chunks x N/16 x ceil(min(M, 64)/16), the 16 x 16 x 128
+    // products per K block. It always wins for M <= 4 (the weights streamed once: 1 x 65536 x
+    // 1536 15.8 against 19.2 us); up to 16 rows, where its cost is streaming the weights, unless
+    // one row of 128 x 256 main-kernel tiles already fills the CUs (M = 8 and 16 with 65536 x
+    // 1536 weights: 17.5 against 18.5 us); from 17 rows while W stays within a limit that grows
+    // with K and is lower where the main kernel has no promote (routes MX and PT). Measured
+    // limits (BS / MX, PT): 2048 / 2048 below K = 1024, 3072 / 2048 below K = 2048, 4096 / 3072
+    // from there. Examples, main kernel against small-M kernel: BS M = 128, 512 x 2048 weights:
+    // 13.5 against 4.4 us (W = 256); BS M = 64, 16384 x 512: 6.2 against 8.2 (W = 4096, K = 512);
+    // BS M = 64, 16384 x 4096: 23.2 against 22.1 (W = 4096); BS M = 256, 4096 x 2048: 13.7
+    // against 12.9 (W = 4096), M = 384: 14.0 against 18.4; MX M = 64, 16384 x 2048: 11.3 against
+    // 14.5 (W = 4096); 7168 x 7168, M = 128: 38.1 against 31.7 (BS, W = 3584), 31.1 against 32.0
+    // (MX); BS M = 64, 28672 x 8192: 43.3 against 59.5 (W = 7168).
+    if (small_m_rows_ok(M)) {
+        if (M <= 4)
             return small_m_config();
+        if (M <= 16) {
+            if (!(N % 256 == 0 && N / 256 >= kCUs))
+                return small_m_config();
+        } else {
+            const int64_t W = (int64_t)((M + fp8bs::kDecodeMaxRows - 1) / fp8bs::kDecodeMaxRows) * (N / 16) *
+                              ((std::min(M, fp8bs::kDecodeMaxRows) + 15) / 16);
+            const bool lean = route == fp8bs::kRouteMX || route == fp8bs::kRoutePT;
+            const int64_t limit = K >= 2048 ? (lean ? 3072 : 4096) : K >= 1024 ? (lean ? 2048 : 3072) : 2048;
+            if (W <= limit)
+                return small_m_config();
+        }
     }
-    // More rows over deep K while the main kernel's 128-row tiles would cover at most a quarter
-    // of the CUs (an eighth for route MX, whose main kernel has no promote): the small-M kernel
-    // in 64-row chunks, each chunk streaming the weights again (2048 x 7168 weights, M = 96 to
-    // 512: 7.4-29.4 us against 38 us; 7168 x 7168, M = 128: 31.7 against 38.1 us, but M = 192:
-    // 46.6 against 38.7; over K = 768 or 1280 the main kernel wins from M = 96; route MX,
-    // 2048 x 7168, M = 256: 15.3 against 30.8 us, 7168 x 7168, M = 128: 32.0 against 31.1).
-    if (M > fp8bs::kDecodeMaxRows && K >= 4096 &&
-        tiles(128, N % 128 == 0 ? 128 : 64) <= (route == fp8bs::kRouteMX ? kCUs / 8 : kCUs / 4) &&
-        small_m_rows_ok(M))
-        return small_m_config();
     if ((route == fp8bs::kRouteMX || route == fp8bs::kRoutePT) && N % 128 != 0)
         return cfg(7, 64);
+    auto rounds = [&](int bm, int bn) { return (tiles(bm, bn) + kCUs - 1) / kCUs; };
     // when one row of 128-row tiles covers M, 256-row tiles would only add padding: 128 x 256
-    // (warp-specialised) where those fill the CUs, else 128 x 128 (M = 64: 65536 x 1536 weights
-    // 18.9 us against 27 us with 256 x 128 tiles; 32768 x 1536 11.5 against 15.3 us; 32768 x
-    // 7168 39.7 against 55.3 us)
+    // (warp-specialised) where those fill the CUs or need fewer rounds of them, else 128 x 128
+    // (M = 64: 65536 x 1536 weights 18.9 us against 27 us with 256 x 128 tiles; 32768 x 1536
+    // 11.5 against 15.3 us; 32768 x 7168 39.7 against 55.3 us; 36864 x 7168, 144 tiles of
+    // 128 x 256 in one round against 288 of 128 x 128 in two: 49.1 against 74.7 us)
     if (M <= 128)
-        return N % 256 == 0 && tiles(128, 256) >= kCUs ? cfg(14, 256) : cfg(0, 128);
+        return N % 256 == 0 && (tiles(128, 256) >= kCUs || rounds(128, 256) < rounds(128, 128)) ? cfg(14, 256)
+                                                                                                : cfg(0, 128);
     // 256 x 256 tiles from two rounds of the CUs; route MX from one (65536 x 1536 weights,
     // M = 256: 28.3 against 32.0 us with 256 x 128 tiles; route BS, 24576 x 1536, M = 1024:
     // 51.4 against 42.5)
@@ -160,7 +170,6 @@ fp8bs_config select(int route, int M, int N, int K)
     // 128x128 tiles, unless they would need more rounds of the CUs than the larger ones (7168 x
     // 7168 weights, M = 640: 280 tiles in two rounds, 74.6 us, against 168 tiles of 256 x 128 in
     // one, 46.1 us)
-    auto rounds = [&](int bm, int bn) { return (tiles(bm, bn) + kCUs - 1) / kCUs; };
     if (rounds(256, 128) < rounds(128, 128))
         return cfg(13, 128);
     if (N % 256 == 0 && rounds(128, 256) < rounds(128, 128))

@@ -93,28 +93,32 @@ def test_select_config_is_shape_driven(fb):
     assert (nn.block_m, nn.block_n, nn.waves_m, nn.waves_n, nn.stages, nn.pingpong) == (256, 128, 4, 2, 3, 2)
     nn16 = fb.fp8bs_select_config(fb.ROUTE_BS, 16384, 1536, 7168)
     assert (nn16.block_m, nn16.block_n, nn16.pingpong) == (256, 128, 2)
-    mx = fb.fp8bs_select_config(fb.ROUTE_MX, 128, 192, 256)
-    assert 192 % mx.block_n == 0
+    mx = fb.fp8bs_select_config(fb.ROUTE_MX, 4096, 192, 256)  # N % 128 != 0: the 128x64 tile
+    assert (mx.small_m, mx.block_n) == (0, 64)
     wide = fb.fp8bs_select_config(fb.ROUTE_BS, 4096, 65536, 1536)  # 1024-tile bands: round-local order
     assert (wide.block_m, wide.block_n) == (256, 256) and wide.xcd_remap == 2
     for route, shape in ((fb.ROUTE_BS, (4096, 65536, 1536)), (fb.ROUTE_MX, (16384, 8192, 1280)),
                          (fb.ROUTE_BS, (128, 256, 512)), (fb.ROUTE_BS, (1, 128, 128))):
         c = fb.fp8bs_select_config(route, *shape)
         assert c.small_m == 1 or (shape[1] % c.block_n == 0 and c.group_m >= 1)
-    # few rows (the decode regime): the small-M kernel for routes BS and PT when M <= 4, up to
-    # 16 rows unless one row of 128x256 tiles fills the 256 CUs, up to 64 rows unless one row of
-    # 128x128 tiles does; beyond 64 rows (in 64-row chunks) over K >= 4096 while 128x128 tiles
-    # would cover at most a quarter of the CUs
+    # the small-M kernel for M <= 4, and otherwise while its 16x16x128 products per K block,
+    # W = ceil(M/64) * N/16 * ceil(min(M, 64)/16), stay within a limit that grows with K: route
+    # BS 2048 below K = 1024, 3072 below K = 2048, 4096 from there; routes MX and PT 2048 below
+    # K = 2048, 3072 from there
     for route, shape, small in ((fb.ROUTE_BS, (1, 128, 128), 1), (fb.ROUTE_BS, (4, 65536, 1536), 1),
                                 (fb.ROUTE_BS, (16, 65536, 1536), 0), (fb.ROUTE_BS, (16, 32768, 1536), 1),
-                                (fb.ROUTE_BS, (17, 32768, 1536), 0), (fb.ROUTE_BS, (64, 16384, 1536), 1),
+                                (fb.ROUTE_BS, (17, 32768, 1536), 0), (fb.ROUTE_BS, (64, 16384, 1536), 0),
                                 (fb.ROUTE_BS, (64, 2048, 7168), 1), (fb.ROUTE_BS, (64, 65536, 1536), 0),
                                 (fb.ROUTE_BS, (65, 128, 7168), 1), (fb.ROUTE_PT, (33, 4096, 512), 1),
                                 (fb.ROUTE_BS, (512, 2048, 7168), 1), (fb.ROUTE_PT, (96, 1536, 7168), 1),
                                 (fb.ROUTE_BS, (640, 2048, 7168), 0), (fb.ROUTE_BS, (192, 7168, 7168), 0),
                                 (fb.ROUTE_BS, (96, 7168, 768), 0), (fb.ROUTE_MX, (128, 2048, 7168), 1),
                                 (fb.ROUTE_MX, (128, 7168, 7168), 0), (fb.ROUTE_MX, (64, 32768, 1536), 0),
-                                (fb.ROUTE_PT, (0, 4096, 512), 0), (fb.ROUTE_MX, (64, 4096, 512), 1)):
+                                (fb.ROUTE_PT, (0, 4096, 512), 0), (fb.ROUTE_MX, (64, 4096, 512), 1),
+                                (fb.ROUTE_BS, (128, 2048, 1024), 1), (fb.ROUTE_BS, (256, 4096, 2048), 1),
+                                (fb.ROUTE_BS, (384, 4096, 2048), 0), (fb.ROUTE_PT, (100, 4096, 512), 1),
+                                (fb.ROUTE_MX, (192, 4096, 2048), 1), (fb.ROUTE_MX, (256, 4096, 2048), 0),
+                                (fb.ROUTE_BS, (48, 16384, 1024), 1), (fb.ROUTE_BS, (64, 16384, 1024), 0)):
         c = fb.fp8bs_select_config(route, *shape)
         assert c.small_m == small, (route, shape)
         if small:
@@ -125,12 +129,15 @@ def test_select_config_is_shape_driven(fb):
         c = fb.fp8bs_select_config(route, *shape)
         assert (c.block_m, c.block_n, c.pingpong) == (128, 256, 2), (route, shape)
     # otherwise 128x128 (one row of 128-row tiles never needs 256-row tiles)
-    for route, shape in ((fb.ROUTE_BS, (64, 32768, 1536)), (fb.ROUTE_BS, (128, 2048, 1024)),
-                         (fb.ROUTE_MX, (128, 32768, 1536)), (fb.ROUTE_PT, (100, 4096, 512))):
+    for route, shape in ((fb.ROUTE_BS, (64, 32768, 1536)), (fb.ROUTE_BS, (128, 7168, 1024)),
+                         (fb.ROUTE_MX, (128, 32768, 1536)), (fb.ROUTE_PT, (100, 7168, 512))):
         c = fb.fp8bs_select_config(route, *shape)
         assert (c.block_m, c.block_n, c.pingpong) == (128, 128, 0), (route, shape)
     c = fb.fp8bs_select_config(fb.ROUTE_BS, 129, 65536, 1536)
     assert c.block_m == 256
+    # one row of 128-row tiles, where 128x256 tiles need one round of the CUs and 128x128 two
+    c = fb.fp8bs_select_config(fb.ROUTE_BS, 64, 36864, 7168)
+    assert (c.block_m, c.block_n, c.pingpong) == (128, 256, 2)
     # 256x256 tiles from one round of the CUs for route MX, from two for the others
     assert (fb.fp8bs_select_config(fb.ROUTE_MX, 256, 65536, 1536).block_m,
             fb.fp8bs_select_config(fb.ROUTE_BS, 1024, 24576, 1536).block_n) == (256, 128)

@@ -168,10 +168,12 @@ def test_plain_entry_picks_small_m(fb, oracle):
 
 
 @pytest.mark.parametrize("route,M,N,K", [("bs", 200, 2048, 4096), ("pt", 130, 1536, 4608), ("mx", 128, 2048, 4096),
-                                         ("mx", 64, 512, 1280)])
+                                         ("mx", 64, 512, 1280), ("bs", 128, 256, 512), ("bs", 256, 1024, 2048),
+                                         ("pt", 192, 512, 1024), ("mx", 256, 1024, 2048)])
 def test_plain_entry_small_m_routes(fb, oracle, route, M, N, K):
-    """Shapes on which the plain entry points select the small-M kernel (64-row chunks over deep
-    K; route MX on its packed activation scales): full-C parity with the oracle."""
+    """Shapes on which the plain entry points select the small-M kernel (64-row chunks while the
+    main kernel's grid would be small; route MX on its packed activation scales): full-C parity
+    with the oracle."""
     rid = {"bs": fb.ROUTE_BS, "pt": fb.ROUTE_PT, "mx": fb.ROUTE_MX}[route]
     assert fb.fp8bs_select_config(rid, M, N, K).small_m == 1, (route, M, N, K)
     C = torch.empty((M, N), dtype=torch.bfloat16, device=dev())

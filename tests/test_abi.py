@@ -128,11 +128,15 @@ def test_select_config_is_shape_driven(fb):
                          (fb.ROUTE_PT, (64, 65536, 7168)), (fb.ROUTE_MX, (64, 65536, 1536))):
         c = fb.fp8bs_select_config(route, *shape)
         assert (c.block_m, c.block_n, c.pingpong) == (128, 256, 2), (route, shape)
-    # otherwise 128x128 (one row of 128-row tiles never needs 256-row tiles)
-    for route, shape in ((fb.ROUTE_BS, (64, 32768, 1536)), (fb.ROUTE_BS, (128, 7168, 1024)),
-                         (fb.ROUTE_MX, (128, 32768, 1536)), (fb.ROUTE_PT, (100, 7168, 512))):
+    # otherwise 128x128 (one row of 128-row tiles never needs 256-row tiles), or 128x64 where
+    # 128x128 tiles would leave CUs idle and 128x64 ones still fit in one round
+    for route, shape in ((fb.ROUTE_BS, (64, 32768, 1536)), (fb.ROUTE_MX, (128, 32768, 1536))):
         c = fb.fp8bs_select_config(route, *shape)
         assert (c.block_m, c.block_n, c.pingpong) == (128, 128, 0), (route, shape)
+    for route, shape in ((fb.ROUTE_BS, (128, 7168, 1024)), (fb.ROUTE_PT, (100, 7168, 512)),
+                         (fb.ROUTE_MX, (128, 7168, 7168)), (fb.ROUTE_BS, (64, 16384, 1536))):
+        c = fb.fp8bs_select_config(route, *shape)
+        assert (c.block_m, c.block_n, c.pingpong) == (128, 64, 0), (route, shape)
     c = fb.fp8bs_select_config(fb.ROUTE_BS, 129, 65536, 1536)
     assert c.block_m == 256
     # one row of 128-row tiles, where 128x256 tiles need one round of the CUs and 128x128 two
@@ -141,9 +145,11 @@ def test_select_config_is_shape_driven(fb):
     # 256x256 tiles from one round of the CUs for route MX, from two for the others
     assert (fb.fp8bs_select_config(fb.ROUTE_MX, 256, 65536, 1536).block_m,
             fb.fp8bs_select_config(fb.ROUTE_BS, 1024, 24576, 1536).block_n) == (256, 128)
-    # 128x128 tiles only while they need no more rounds of the CUs than 256x128 tiles
+    # 128x128 tiles only while they need no more rounds of the CUs than 256x128 tiles, and
+    # 128x64 while those fit in one round
     for shape, tile in (((640, 7168, 7168), (256, 128)), ((1024, 7168, 7168), (256, 128)),
-                        ((1024, 2048, 7168), (128, 128)), ((200, 4096, 512), (128, 128))):
+                        ((1024, 3072, 7168), (128, 128)), ((1024, 2048, 7168), (128, 64)),
+                        ((200, 4096, 512), (128, 64))):
         c = fb.fp8bs_select_config(fb.ROUTE_BS, *shape)
         assert (c.block_m, c.block_n) == tile, shape
 

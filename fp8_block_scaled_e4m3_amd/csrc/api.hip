@@ -114,21 +114,21 @@ fp8bs_config select(int route, int M, int N, int K)
         return make_config(variant, group_m, xcd, 1);
     };
     // The small-M kernel against the main kernel. With few rows the main kernel runs one round
-    // of 128-row tiles whose time is set by the K loop (about 3.7 us + 0.6 us per K block), while
-    // the small-M kernel splits K over its waves and spreads the work over chunks x N/16
-    // workgroups: its time grows with W = chunks x N/16 x ceil(min(M, 64)/16), the 16 x 16 x 128
-    // products per K block. It always wins for M <= 4 (the weights streamed once: 1 x 65536 x
-    // 1536 15.8 against 19.2 us); up to 16 rows, where its cost is streaming the weights, unless
-    // one row of 128 x 256 main-kernel tiles already fills the CUs (M = 8 and 16 with 65536 x
-    // 1536 weights: 17.5 against 18.5 us); from 17 rows while W stays within a limit that grows
-    // with K and is lower where the main kernel has no promote (routes MX and PT). Measured
-    // limits (BS / MX, PT): 2048 / 2048 below K = 1024, 3072 / 2048 below K = 2048, 4096 / 3072
-    // from there. Examples, main kernel against small-M kernel: BS M = 128, 512 x 2048 weights:
-    // 13.5 against 4.4 us (W = 256); BS M = 64, 16384 x 512: 6.2 against 8.2 (W = 4096, K = 512);
-    // BS M = 64, 16384 x 4096: 23.2 against 22.1 (W = 4096); BS M = 256, 4096 x 2048: 13.7
-    // against 12.9 (W = 4096), M = 384: 14.0 against 18.4; MX M = 64, 16384 x 2048: 11.3 against
-    // 14.5 (W = 4096); 7168 x 7168, M = 128: 38.1 against 31.7 (BS, W = 3584), 31.1 against 32.0
-    // (MX); BS M = 64, 28672 x 8192: 43.3 against 59.5 (W = 7168).
+    // of 128-row tiles whose time is set by the K loop (warp-specialised 128 x 128 tiles, route
+    // BS: about 3.7 us + 0.47 us per K block, whatever N), while the small-M kernel splits K over its waves
+    // and spreads the work over chunks x N/16 workgroups: its time grows with W = chunks x N/16 x
+    // ceil(min(M, 64)/16), the 16 x 16 x 128 products per K block. It always wins for M <= 4
+    // (the weights streamed once: 1 x 65536 x 1536 15.8 against 19.2 us); up to 16 rows, where
+    // its cost is streaming the weights, unless one row of 128 x 256 main-kernel tiles already
+    // fills the CUs (M = 8 and 16 with 65536 x 1536 weights: 17.5 against 18.5 us); from 17 rows
+    // while W stays within a limit: 3072 for route BS from K = 2048, else 2048 (routes MX and PT,
+    // whose main kernel has no promote, and route BS below K = 2048). Examples, main kernel
+    // against small-M kernel: BS M = 128, 2048 x 2048 weights: 11.2 against 4.2 us (W = 1024);
+    // BS M = 384, 2048 x 2048: 11.2 against 9.9 (W = 3072), M = 512: 11.3 against 12.8 (W =
+    // 4096); BS M = 48, 16384 x 1024: 7.2 against 8.4 (W = 3072, K = 1024); BS M = 128, 7168 x
+    // 7168: 29.9 against 31.5 (W = 3584); MX M = 128, 2048 x 2048: 9.2 against 4.4 (W = 1024),
+    // M = 192, 4096 x 4096: 14.8 against 17.2 (W = 3072); PT M = 192, 4096 x 4096: 14.2 against
+    // 16.6; BS M = 64, 28672 x 8192: 43.3 against 59.5 (W = 7168).
     if (small_m_rows_ok(M)) {
         if (M <= 4)
             return small_m_config();
@@ -139,7 +139,7 @@ fp8bs_config select(int route, int M, int N, int K)
             const int64_t W = (int64_t)((M + fp8bs::kDecodeMaxRows - 1) / fp8bs::kDecodeMaxRows) * (N / 16) *
                               ((std::min(M, fp8bs::kDecodeMaxRows) + 15) / 16);
             const bool lean = route == fp8bs::kRouteMX || route == fp8bs::kRoutePT;
-            const int64_t limit = K >= 2048 ? (lean ? 3072 : 4096) : K >= 1024 ? (lean ? 2048 : 3072) : 2048;
+            const int64_t limit = !lean && K >= 2048 ? 3072 : 2048;
             if (W <= limit)
                 return small_m_config();
         }
@@ -147,11 +147,12 @@ fp8bs_config select(int route, int M, int N, int K)
     if ((route == fp8bs::kRouteMX || route == fp8bs::kRoutePT) && N % 128 != 0)
         return cfg(7, 64);
     auto rounds = [&](int bm, int bn) { return (tiles(bm, bn) + kCUs - 1) / kCUs; };
-    // 128 x 128 tiles that leave CUs idle: 128 x 64 tiles instead while those still fit in one
-    // round. Such grids are bound by each tile's K loop, so twice the tiles cost no more time per
-    // tile and each tile's loop is lighter (route MX, 512 x 2048 x 7168: 28.0 against 31.2 us;
-    // route BS, 1024 x 2048 x 7168: 37.0 against 39.0, 512 x 4096 x 4096: 23.1 against 24.1)
-    auto square = [&]() { return tiles(128, 64) <= kCUs ? cfg(7, 64) : cfg(0, 128); };
+    // 128 x 128 tiles in one round of the CUs: warp-specialised (four math waves, one per SIMD,
+    // beside four loader waves). Such grids are bound by each tile's K loop, which the loader
+    // waves shorten: BS 512 x 7168 x 7168 31.8 us against 39.4 with every wave loading (and 39.6
+    // with 128 x 64 tiles), 1024 x 3072 x 7168 31.4 against 39.3, 128 x 16384 x 1536 9.8 against
+    // 11.5; MX 512 x 7168 x 7168 26.5 against 32.1, 1024 x 2048 x 7168 24.3 against 31.1.
+    auto square = [&]() { return tiles(128, 128) <= kCUs ? cfg(16, 128) : cfg(0, 128); };
     // when one row of 128-row tiles covers M, 256-row tiles would only add padding: 128 x 256
     // (warp-specialised) where those fill the CUs or need fewer rounds of them, else 128 x 128
     // (M = 64: 65536 x 1536 weights 18.9 us against 27 us with 256 x 128 tiles; 32768 x 1536
@@ -160,10 +161,13 @@ fp8bs_config select(int route, int M, int N, int K)
     if (M <= 128)
         return N % 256 == 0 && (tiles(128, 256) >= kCUs || rounds(128, 256) < rounds(128, 128)) ? cfg(14, 256)
                                                                                                 : square();
-    // 256 x 256 tiles from two rounds of the CUs; route MX from one (65536 x 1536 weights,
-    // M = 256: 28.3 against 32.0 us with 256 x 128 tiles; route BS, 24576 x 1536, M = 1024:
-    // 51.4 against 42.5)
-    if (N % 256 == 0 && tiles(256, 256) >= (route == fp8bs::kRouteMX ? 1 : 2) * kCUs)
+    // 256 x 256 tiles when they fill at least one round of the CUs and their rounds, each as
+    // long as two of 256 x 128 tiles, are no more than those tiles would need (65536 x 1536
+    // weights, M = 256: one round, MX 28.3 against 32.0 us with 256 x 128 tiles; route BS,
+    // 24576 x 1536, M = 1024: 384 tiles in two rounds, 51.4 against 42.5 for 768 of 256 x 128
+    // in three; 36864 x 7168, M = 1024: 576 tiles in three rounds, 286.7 against 258.6 for 1152
+    // in five)
+    if (N % 256 == 0 && tiles(256, 256) >= kCUs && 2 * rounds(256, 256) <= rounds(256, 128))
         return cfg(2, 256);
     // the 256x128 / 128x256 tiles run warp-specialised (four loader waves beside the eight
     // math waves): measured 5-7% faster than the same tiles with every wave loading on the

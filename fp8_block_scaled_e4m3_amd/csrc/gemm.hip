@@ -897,7 +897,8 @@ static hipError_t launch_tile(const GemmArgs& a, const GemmConfig& c)
     X(12, 128, 256, 2, 4, 2, 1)  \
     X(13, 256, 128, 4, 2, 3, 2)  \
     X(14, 128, 256, 2, 4, 3, 2)  \
-    X(15, 256, 128, 2, 2, 3, 2)
+    X(15, 256, 128, 2, 2, 3, 2)  \
+    X(16, 128, 128, 2, 2, 3, 2)
 
 const VariantInfo* variant_info(int v)
 {

@@ -101,24 +101,24 @@ def test_select_config_is_shape_driven(fb):
                          (fb.ROUTE_BS, (128, 256, 512)), (fb.ROUTE_BS, (1, 128, 128))):
         c = fb.fp8bs_select_config(route, *shape)
         assert c.small_m == 1 or (shape[1] % c.block_n == 0 and c.group_m >= 1)
-    # the small-M kernel for M <= 4, and otherwise while its 16x16x128 products per K block,
-    # W = ceil(M/64) * N/16 * ceil(min(M, 64)/16), stay within a limit that grows with K: route
-    # BS 2048 below K = 1024, 3072 below K = 2048, 4096 from there; routes MX and PT 2048 below
-    # K = 2048, 3072 from there
+    # the small-M kernel for M <= 4; up to 16 rows unless one row of 128x256 tiles fills the
+    # CUs; from 17 rows while its 16x16x128 products per K block, W = ceil(M/64) * N/16 *
+    # ceil(min(M, 64)/16), stay within 3072 (route BS from K = 2048) or 2048 (otherwise)
     for route, shape, small in ((fb.ROUTE_BS, (1, 128, 128), 1), (fb.ROUTE_BS, (4, 65536, 1536), 1),
                                 (fb.ROUTE_BS, (16, 65536, 1536), 0), (fb.ROUTE_BS, (16, 32768, 1536), 1),
                                 (fb.ROUTE_BS, (17, 32768, 1536), 0), (fb.ROUTE_BS, (64, 16384, 1536), 0),
                                 (fb.ROUTE_BS, (64, 2048, 7168), 1), (fb.ROUTE_BS, (64, 65536, 1536), 0),
                                 (fb.ROUTE_BS, (65, 128, 7168), 1), (fb.ROUTE_PT, (33, 4096, 512), 1),
-                                (fb.ROUTE_BS, (512, 2048, 7168), 1), (fb.ROUTE_PT, (96, 1536, 7168), 1),
+                                (fb.ROUTE_BS, (512, 2048, 7168), 0), (fb.ROUTE_PT, (96, 1536, 7168), 1),
                                 (fb.ROUTE_BS, (640, 2048, 7168), 0), (fb.ROUTE_BS, (192, 7168, 7168), 0),
                                 (fb.ROUTE_BS, (96, 7168, 768), 0), (fb.ROUTE_MX, (128, 2048, 7168), 1),
                                 (fb.ROUTE_MX, (128, 7168, 7168), 0), (fb.ROUTE_MX, (64, 32768, 1536), 0),
                                 (fb.ROUTE_PT, (0, 4096, 512), 0), (fb.ROUTE_MX, (64, 4096, 512), 1),
-                                (fb.ROUTE_BS, (128, 2048, 1024), 1), (fb.ROUTE_BS, (256, 4096, 2048), 1),
-                                (fb.ROUTE_BS, (384, 4096, 2048), 0), (fb.ROUTE_PT, (100, 4096, 512), 1),
-                                (fb.ROUTE_MX, (192, 4096, 2048), 1), (fb.ROUTE_MX, (256, 4096, 2048), 0),
-                                (fb.ROUTE_BS, (48, 16384, 1024), 1), (fb.ROUTE_BS, (64, 16384, 1024), 0)):
+                                (fb.ROUTE_BS, (128, 2048, 1024), 1), (fb.ROUTE_BS, (384, 2048, 2048), 1),
+                                (fb.ROUTE_BS, (256, 4096, 2048), 0), (fb.ROUTE_PT, (100, 4096, 512), 1),
+                                (fb.ROUTE_MX, (128, 4096, 2048), 1), (fb.ROUTE_MX, (192, 4096, 2048), 0),
+                                (fb.ROUTE_BS, (48, 7168, 1024), 1), (fb.ROUTE_BS, (48, 16384, 1024), 0),
+                                (fb.ROUTE_BS, (200, 2048, 4096), 1), (fb.ROUTE_PT, (192, 4096, 4096), 0)):
         c = fb.fp8bs_select_config(route, *shape)
         assert c.small_m == small, (route, shape)
         if small:
@@ -128,15 +128,15 @@ def test_select_config_is_shape_driven(fb):
                          (fb.ROUTE_PT, (64, 65536, 7168)), (fb.ROUTE_MX, (64, 65536, 1536))):
         c = fb.fp8bs_select_config(route, *shape)
         assert (c.block_m, c.block_n, c.pingpong) == (128, 256, 2), (route, shape)
-    # otherwise 128x128 (one row of 128-row tiles never needs 256-row tiles), or 128x64 where
-    # 128x128 tiles would leave CUs idle and 128x64 ones still fit in one round
-    for route, shape in ((fb.ROUTE_BS, (64, 32768, 1536)), (fb.ROUTE_MX, (128, 32768, 1536))):
-        c = fb.fp8bs_select_config(route, *shape)
-        assert (c.block_m, c.block_n, c.pingpong) == (128, 128, 0), (route, shape)
-    for route, shape in ((fb.ROUTE_BS, (128, 7168, 1024)), (fb.ROUTE_PT, (100, 7168, 512)),
+    # otherwise 128x128 (one row of 128-row tiles never needs 256-row tiles), warp-specialised
+    # when those tiles fit in one round of the CUs
+    for route, shape in ((fb.ROUTE_BS, (64, 32768, 1536)), (fb.ROUTE_MX, (128, 32768, 1536)),
+                         (fb.ROUTE_BS, (128, 7168, 1024)), (fb.ROUTE_PT, (100, 7168, 512)),
                          (fb.ROUTE_MX, (128, 7168, 7168)), (fb.ROUTE_BS, (64, 16384, 1536))):
         c = fb.fp8bs_select_config(route, *shape)
-        assert (c.block_m, c.block_n, c.pingpong) == (128, 64, 0), (route, shape)
+        assert (c.block_m, c.block_n, c.waves_m, c.waves_n, c.pingpong) == (128, 128, 2, 2, 2), (route, shape)
+    c = fb.fp8bs_select_config(fb.ROUTE_BS, 64, 40960 - 128, 1536)  # 319 tiles: two rounds
+    assert (c.block_m, c.block_n, c.pingpong) == (128, 128, 0)
     c = fb.fp8bs_select_config(fb.ROUTE_BS, 129, 65536, 1536)
     assert c.block_m == 256
     # one row of 128-row tiles, where 128x256 tiles need one round of the CUs and 128x128 two
@@ -145,11 +145,10 @@ def test_select_config_is_shape_driven(fb):
     # 256x256 tiles from one round of the CUs for route MX, from two for the others
     assert (fb.fp8bs_select_config(fb.ROUTE_MX, 256, 65536, 1536).block_m,
             fb.fp8bs_select_config(fb.ROUTE_BS, 1024, 24576, 1536).block_n) == (256, 128)
-    # 128x128 tiles only while they need no more rounds of the CUs than 256x128 tiles, and
-    # 128x64 while those fit in one round
+    # 128x128 tiles only while they need no more rounds of the CUs than 256x128 tiles
     for shape, tile in (((640, 7168, 7168), (256, 128)), ((1024, 7168, 7168), (256, 128)),
-                        ((1024, 3072, 7168), (128, 128)), ((1024, 2048, 7168), (128, 64)),
-                        ((200, 4096, 512), (128, 64))):
+                        ((1024, 3072, 7168), (128, 128)), ((1024, 2048, 7168), (128, 128)),
+                        ((200, 4096, 512), (128, 128))):
         c = fb.fp8bs_select_config(fb.ROUTE_BS, *shape)
         assert (c.block_m, c.block_n) == tile, shape
 

@@ -559,10 +559,9 @@ def main() -> int:
                     forced.small_m = 1
                     # the main kernel's tile for one row of 128-row tiles, as the selector takes it:
                     # 128x256 where those fill the CUs or need fewer rounds of them than 128x128,
+                    # else 128x128 (both warp-specialised)
                     wide = dc.N % 256 == 0 and (dc.N // 256 >= 256 or -(-dc.N // 256 // 256) < -(-dc.N // 128 // 256))
-                    # 128x128 warp-specialised while those tiles fit in one round of the CUs
-                    pp = 2 if dc.N // 128 <= 256 else 0
-                    main_cfg = fb.Config(128, 256, 2, 4, 3, 4, 1, 1, 2) if wide else fb.Config(128, 128, 2, 2, 3, 4, 1, 1, pp)
+                    main_cfg = fb.Config(128, 256, 2, 4, 3, 4, 1, 1, 2) if wide else fb.Config(128, 128, 2, 2, 3, 4, 1, 1, 2)
                     for key, c in (("small_m_kernel", forced), ("main_kernel", main_cfg)):
                         dc.launch = lambda dc=dc, c=c: fb.fp8bs_gemm_with_config(
                             dc.A, dc.sa, dc.B, dc.sb, dc.C, c, stream)

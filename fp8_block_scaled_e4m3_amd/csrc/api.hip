@@ -147,12 +147,13 @@ fp8bs_config select(int route, int M, int N, int K)
     if ((route == fp8bs::kRouteMX || route == fp8bs::kRoutePT) && N % 128 != 0)
         return cfg(7, 64);
     auto rounds = [&](int bm, int bn) { return (tiles(bm, bn) + kCUs - 1) / kCUs; };
-    // 128 x 128 tiles in one round of the CUs: warp-specialised (four math waves, one per SIMD,
-    // beside four loader waves). Such grids are bound by each tile's K loop, which the loader
-    // waves shorten: BS 512 x 7168 x 7168 31.8 us against 39.4 with every wave loading (and 39.6
-    // with 128 x 64 tiles), 1024 x 3072 x 7168 31.4 against 39.3, 128 x 16384 x 1536 9.8 against
-    // 11.5; MX 512 x 7168 x 7168 26.5 against 32.1, 1024 x 2048 x 7168 24.3 against 31.1.
-    auto square = [&]() { return tiles(128, 128) <= kCUs ? cfg(16, 128) : cfg(0, 128); };
+    // 128 x 128 tiles run warp-specialised (four math waves, one per SIMD, beside four loader
+    // waves). Grids of one round are bound by each tile's K loop, which the loader waves shorten:
+    // BS 512 x 7168 x 7168 31.8 us against 39.4 with every wave loading (and 39.6 with 128 x 64
+    // tiles), 1024 x 3072 x 7168 31.4 against 39.3, 128 x 16384 x 1536 9.8 against 11.5; MX
+    // 512 x 7168 x 7168 26.5 against 32.1, 1024 x 2048 x 7168 24.3 against 31.1; with more
+    // rounds too (BS 1024 x 16384 x 1536: 32.0 against 38.9).
+    auto square = [&]() { return cfg(16, 128); };
     // when one row of 128-row tiles covers M, 256-row tiles would only add padding: 128 x 256
     // (warp-specialised) where those fill the CUs or need fewer rounds of them, else 128 x 128
     // (M = 64: 65536 x 1536 weights 18.9 us against 27 us with 256 x 128 tiles; 32768 x 1536

@@ -128,15 +128,14 @@ def test_select_config_is_shape_driven(fb):
                          (fb.ROUTE_PT, (64, 65536, 7168)), (fb.ROUTE_MX, (64, 65536, 1536))):
         c = fb.fp8bs_select_config(route, *shape)
         assert (c.block_m, c.block_n, c.pingpong) == (128, 256, 2), (route, shape)
-    # otherwise 128x128 (one row of 128-row tiles never needs 256-row tiles), warp-specialised
-    # when those tiles fit in one round of the CUs
+    # otherwise 128x128, warp-specialised (one row of 128-row tiles never needs 256-row tiles)
     for route, shape in ((fb.ROUTE_BS, (64, 32768, 1536)), (fb.ROUTE_MX, (128, 32768, 1536)),
                          (fb.ROUTE_BS, (128, 7168, 1024)), (fb.ROUTE_PT, (100, 7168, 512)),
                          (fb.ROUTE_MX, (128, 7168, 7168)), (fb.ROUTE_BS, (64, 16384, 1536))):
         c = fb.fp8bs_select_config(route, *shape)
         assert (c.block_m, c.block_n, c.waves_m, c.waves_n, c.pingpong) == (128, 128, 2, 2, 2), (route, shape)
     c = fb.fp8bs_select_config(fb.ROUTE_BS, 64, 40960 - 128, 1536)  # 319 tiles: two rounds
-    assert (c.block_m, c.block_n, c.pingpong) == (128, 128, 0)
+    assert (c.block_m, c.block_n, c.pingpong) == (128, 128, 2)
     c = fb.fp8bs_select_config(fb.ROUTE_BS, 129, 65536, 1536)
     assert c.block_m == 256
     # one row of 128-row tiles, where 128x256 tiles need one round of the CUs and 128x128 two

@@ -173,6 +173,12 @@ fp8bs_config select(int route, int M, int N, int K)
     // the 256x128 / 128x256 tiles run warp-specialised (four loader waves beside the eight
     // math waves): measured 5-7% faster than the same tiles with every wave loading on the
     // 4096 x 2048 x 7168 and 16384 x 1536 x 7168 shapes
+    // 256 x 128 tiles just past one round (257 to 384: two rounds, the second mostly idle):
+    // three rounds of the warp-specialised 128 x 128 tiles finish sooner, a round of those
+    // costing about 1.25x half a round of 256 x 128 tiles (BS 1280 x 7168 x 2048: 30.1 against
+    // 32.5 us, 2304 x 3840 x 4096: 54.0 against 56.9; MX 4352 x 2048 x 7168: 72.9 against 80.3)
+    if (tiles(256, 128) > kCUs && 2 * tiles(256, 128) <= 3 * kCUs)
+        return square();
     if (tiles(256, 128) >= kCUs)
         return cfg(13, 128);
     if (N % 256 == 0 && tiles(128, 256) >= kCUs)

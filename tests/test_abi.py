@@ -136,6 +136,12 @@ def test_select_config_is_shape_driven(fb):
         assert (c.block_m, c.block_n, c.waves_m, c.waves_n, c.pingpong) == (128, 128, 2, 2, 2), (route, shape)
     c = fb.fp8bs_select_config(fb.ROUTE_BS, 64, 40960 - 128, 1536)  # 319 tiles: two rounds
     assert (c.block_m, c.block_n, c.pingpong) == (128, 128, 2)
+    # 256x128 tiles just past one round (257 to 384): 128x128 ones instead; at 256 and from 385
+    # 256x128
+    for route, shape, tile in ((fb.ROUTE_BS, (1280, 7168, 2048), (128, 128)), (fb.ROUTE_MX, (4352, 2048, 7168), (128, 128)),
+                               (fb.ROUTE_BS, (4096, 2048, 7168), (256, 128)), (fb.ROUTE_BS, (1664, 7168, 2048), (256, 128))):
+        c = fb.fp8bs_select_config(route, *shape)
+        assert (c.block_m, c.block_n, c.pingpong) == (*tile, 2), (route, shape)
     c = fb.fp8bs_select_config(fb.ROUTE_BS, 129, 65536, 1536)
     assert c.block_m == 256
     # one row of 128-row tiles, where 128x256 tiles need one round of the CUs and 128x128 two

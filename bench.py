@@ -2,42 +2,40 @@
 
 One step = one fp8bs_gemm launch on the narrow-N, deep-K workload (M=4096, N=2048, K=7168,
 route BS: fp32 per-1x128 activation scales, fp32 per-128x128 weight scales, bf16 out), with
-every input already resident in HBM. Prints ONE JSON line on stdout:
+every input already resident in HBM. Prints ONE JSON line on stdout, compact so that it
+survives a tail of the output whole:
 
-  value        -- TFLOP/s (2*M*N*K per step / wall time per step) of that workload
-  roofline     -- the GEMM kernel's achieved TFLOP/s from HIP events on its own stream,
-                  against the dense fp8 matrix-core peak (5.0 PFLOP/s); traffic from the
-                  committed rocprofv3 counter record when it matches the current kernel source
+  value        -- TFLOP/s (2*M*N*K per step / wall time per step) of that workload over the
+                  counted --steps, after a time-based pre-roll (preroll_ms of launches: the GPU
+                  raises its clock over the first ~20 ms of sustained work) and --warmup launches
+  per_config   -- every workload of workload.CONFIGS: parity of the output against the oracle
+                  (sampled whole rows and columns) checked BEFORE it is timed, then the
+                  minimum over 3 runs of each run's median per-launch time ("us"; each run is 5
+                  groups of back-to-back launches timed by events; "us_med" is the median of
+                  the three), TFLOP/s, fraction of the 5.0 PFLOP/s dense fp8 peak, the
+                  fraction of the 8 TB/s HBM peak for the algorithmic bytes, and the cold time
+                  (single launches after a 1 GiB read evicting L2 and the MALL)
+  roofline     -- the GEMM kernel's achieved TFLOP/s from HIP events on its own stream over the
+                  counted steps, against the dense fp8 peak; traffic from the committed
+                  rocprofv3 counter record when it matches the current kernel source
+  cpu_baseline -- the CPU oracle (fp64, OpenMP) on a bounded sample of the main workload
+  oracle       -- the same oracle timed per workload on a few sampled whole output rows
+  twin         -- the promote-free twin (fp8pt_gemm: one scale per row of A and of B) on the
+                  route-BS shapes: BS time / twin time is the cost of the per-block promote
   mfma_ceiling -- the matrix core's sustained rate on this workload's own operand bytes with
-                  no memory traffic (the gfx950 matrix core slows down when operand bits
-                  change between instructions; this is the reachable ceiling for this data)
-  per_shape    -- steady-state ("hot", back-to-back launches) time of every workload
-                  in workload.CONFIGS, TFLOP/s, % of peak, algorithmic
-                  HBM GB/s, and the "cold" time of single launches that each follow a 1 GiB
-                  write evicting L2 and the MALL
-  ceiling_twin -- the promote-free twin (fp8pt_gemm: one scale per row of A and of B, applied
-                  in the epilogue) on the route-BS shapes: the same matrix work without the
-                  per-block promote; bs_over_twin is the promote's cost as a time ratio
-  quantiser    -- the activation quantisers (bf16 -> e4m3 codes + scales) on the activation
-                  shapes of narrow-N, K-light (route BS) and mxfp8 (route MX): time, GB/s of
-                  algorithmic traffic (2 B read + 1 B written per element, plus scales) and the
-                  fraction of the 8 TB/s HBM peak
-  small_m      -- few activation rows (M = 1, 16, 64: the decode regime) against the weights of
-                  each workload: hot and cold time of the plain entry point, algorithmic GB/s and
-                  fraction of the HBM peak of the cold launch; for route BS also the small-M
-                  kernel and the main kernel (128-row tile) each forced
-  cpu_baseline -- the CPU oracle (fp64, OpenMP) on a bounded sample of output rows
-  parity       -- sampled whole rows and columns of every timed output against the oracle
-                  (16 + 16 for the main workload, 8 + 8 elsewhere)
+                  no memory traffic
+  quantiser, small_m -- compact rows (time, fraction of the HBM peak, parity); the full
+                  records go to stderr
 
-The GPU raises its clock over the first ~20 ms of sustained work, so every measurement is
-preceded by a warmup of that order (the default --warmup covers it for the main workload).
-
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only NAME]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--preroll-ms P] [--no-cpu] [--only NAME]
        python bench.py --profile NAME [--steps K]       (for rocprofv3 runs; also runs a copy
                                                           of known size for counter scaling)
        python bench.py --ingest-counters DIR            (rocprofv3 FETCH_SIZE / WRITE_SIZE
                                                           csv dirs -> profiles/traffic.json)
+       python bench.py --ksweep [--ksweep-shape M,N]    (time vs K for routes BS and PT, with a
+                                                          least-squares fit fixed + slope * K/128)
+       python bench.py --tile-sweep NAME                (every tile order (group_m, XCD mapping)
+                                                          and instantiated tile on one workload)
 """
 from __future__ import annotations
 
@@ -85,18 +83,26 @@ def algorithmic_bytes(route: str, M: int, N: int, K: int) -> int:
 
 
 class Case:
-    """Device-resident operands of one workload plus a launch closure on a given stream."""
+    """Device-resident operands of one workload plus a launch closure on a given stream.
 
-    def __init__(self, name: str, seed: int, stream, twin: bool = False, rows: int | None = None):
+    rows overrides M (the small-M rows); shape=(M, N, K) replaces the workload's shape (the K
+    sweep); config runs the *_with_config entry with that configuration instead of the plain
+    entry point."""
+
+    def __init__(self, name: str, seed: int, stream, twin: bool = False, rows: int | None = None,
+                 shape=None, config=None):
         import torch
 
         import fp8_block_scaled_e4m3_amd as fb
         import workload
 
-        cfg = workload.CONFIGS[name]
+        cfg = workload.CONFIGS[name] if name in workload.CONFIGS else {"route": "bs"}
         self.name, self.route = name, ("pt" if twin else cfg["route"])
-        self.M, self.N, self.K = (rows if rows is not None else cfg["M"]), cfg["N"], cfg["K"]
-        # route MX with fewer than 64 rows: the small-M entry, with row-major activation scales
+        if shape is not None:
+            self.M, self.N, self.K = shape
+        else:
+            self.M, self.N, self.K = (rows if rows is not None else cfg["M"]), cfg["N"], cfg["K"]
+        # route MX with rows not in whole 64-row groups: the small-M entry, row-major activation scales
         small_mx = self.route == "mx" and self.M % 64 != 0
         dev = torch.device("cuda:0")
         t0 = time.time()
@@ -125,17 +131,37 @@ class Case:
                                                  torch.from_numpy(y.b_e8m0).to(dev), stream)
         self.C = torch.empty((self.M, self.N), dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
-        log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s")
-        fn = {"bs": fb.fp8bs_gemm, "mx": fb.fp8mx_gemm_small_m if small_mx else fb.fp8mx_gemm,
-              "pt": fb.fp8pt_gemm}[self.route]
-        self.launch = lambda: fn(self.A, self.sa, self.B, self.sb, self.C, stream)
+        log(f"[bench] {name} {self.route} {self.M}x{self.N}x{self.K}: inputs ready in {time.time() - t0:.1f}s")
         route_id = {"bs": fb.ROUTE_BS, "mx": fb.ROUTE_MX, "pt": fb.ROUTE_PT}[self.route]
-        self.config = {"small_m": 1} if small_mx else \
-            fb.fp8bs_select_config(route_id, self.M, self.N, self.K).as_dict()
+        if config is not None:
+            fn = {"bs": fb.fp8bs_gemm_with_config, "mx": fb.fp8mx_gemm_with_config,
+                  "pt": fb.fp8pt_gemm_with_config}[self.route]
+            self.launch = lambda: fn(self.A, self.sa, self.B, self.sb, self.C, config, stream)
+            self.config = config.as_dict()
+        else:
+            fn = {"bs": fb.fp8bs_gemm, "mx": fb.fp8mx_gemm_small_m if small_mx else fb.fp8mx_gemm,
+                  "pt": fb.fp8pt_gemm}[self.route]
+            self.launch = lambda: fn(self.A, self.sa, self.B, self.sb, self.C, stream)
+            self.config = {"small_m": 1} if small_mx else \
+                fb.fp8bs_select_config(route_id, self.M, self.N, self.K).as_dict()
 
     @property
     def flops(self) -> int:
         return 2 * self.M * self.N * self.K
+
+    def preroll(self, ms: float) -> int:
+        """Launch back to back for at least `ms` milliseconds of wall time (the clock ramp);
+        returns the number of launches."""
+        import torch
+        t0 = time.perf_counter()
+        n = 0
+        while (time.perf_counter() - t0) * 1e3 < ms or n < 3:
+            self.launch()
+            n += 1
+            if n % 16 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        return n
 
     def time_launches(self, steps: int, warmup: int, stream):
         """(wall seconds per launch, event seconds per launch) over exactly `steps` launches
@@ -156,29 +182,37 @@ class Case:
         ev = e0.elapsed_time(e1) / 1e3 / steps
         return wall, ev
 
-    def steady_state(self, stream, warm_s: float = 0.06, time_s: float = 0.06):
-        """Warm up for warm_s seconds of launches, then time about time_s seconds of them."""
+    def repeated(self, stream, preroll_ms: float = 60.0, repeats: int = 3, subruns: int = 5, time_s: float = 0.03):
+        """Pre-roll, then `repeats` runs; each run is `subruns` groups of back-to-back launches,
+        every group between one pair of events on the stream, and yields the median of its
+        groups' per-launch times. Returns (the per-run medians in seconds, launches per group).
+        Whole groups are timed, not single launches, so no event sits between two launches."""
         import torch
         t0 = time.perf_counter()
-        n = 0
-        while time.perf_counter() - t0 < warm_s or n < 5:
-            self.launch()
-            n += 1
-            if n % 16 == 0:
-                torch.cuda.synchronize()
-        torch.cuda.synchronize()
-        per = max((time.perf_counter() - t0) / n, 1e-6)
-        steps = int(min(2000, max(50, time_s / per)))
-        return self.time_launches(steps, 0, stream) + (steps,)
+        n0 = self.preroll(preroll_ms)
+        per = max((time.perf_counter() - t0) / n0, 1e-6)
+        n = int(min(400, max(8, time_s / subruns / per)))
+        medians = []
+        for _ in range(repeats):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(subruns)]
+            for a, b in ev:
+                a.record(stream)
+                for _ in range(n):
+                    self.launch()
+                b.record(stream)
+            torch.cuda.synchronize()
+            t = sorted(a.elapsed_time(b) / 1e3 / n for a, b in ev)
+            medians.append(t[len(t) // 2])
+        return medians, n
 
-    def cold(self, stream, scratch, reps: int = 15):
+    def cold(self, stream, evict, reps: int = 15):
         """Median and min seconds of single launches, each preceded (outside the timed pair of
-        events) by a write of `scratch` large enough to evict L2 and the MALL."""
+        events) by `evict()`, which reads more than L2 and the MALL hold."""
         import torch
         starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
         ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
         for i in range(reps):
-            scratch.fill_(i & 0xFF)
+            evict()
             starts[i].record(stream)
             self.launch()
             ends[i].record(stream)
@@ -243,20 +277,26 @@ def sampled_parity(case: Case, nrows: int = 16, ncols: int = 16) -> dict:
                 passed=bool(bad == 0 and cos >= 0.9999 and np.all(np.isfinite(g))))
 
 
-def cpu_baseline(case: Case, target_s: float = 12.0) -> dict:
-    """The oracle as it stands, on a bounded sample of whole output rows of the workload
-    (all M rows when they take less than target_s)."""
-    import numpy as np
-
+def oracle_run(case: Case):
+    """A closure computing whole output rows of the case with the oracle."""
     import oracle
     o = oracle.load()
     h = case.host
-    run = (lambda rows: o.bs_gemm(h.A, h.a_scale, h.B, h.b_scale, rows=rows)) if case.route == "bs" else \
-        (lambda rows: o.mx_gemm(h.A, h.a_e8m0, h.B, h.b_e8m0, rows=rows))
+    if case.route == "bs":
+        return o, lambda rows: o.bs_gemm(h.A, h.a_scale, h.B, h.b_scale, rows=rows)
+    if case.route == "pt":
+        return o, lambda rows: o.pt_gemm(h.A, h.a_scale, h.B, h.b_scale, rows=rows)
+    return o, lambda rows: o.mx_gemm(h.A, h.a_e8m0, h.B, h.b_e8m0, rows=rows)
+
+
+def oracle_time(case: Case, target_s: float) -> dict:
+    """The oracle as it stands, timed on whole output rows of the workload: a first run on one
+    row per thread sizes a second run of about target_s seconds (all M rows at most)."""
+    import numpy as np
+    o, run = oracle_run(case)
     threads = max(o.num_threads(), 1)
-    probe = np.arange(threads, dtype=np.int32)
     t0 = time.perf_counter()
-    run(probe)
+    run(np.arange(min(threads, case.M), dtype=np.int32))
     dt = time.perf_counter() - t0
     nrows = int(min(case.M, max(threads, threads * round(target_s / max(dt, 1e-3)))))
     rows = np.arange(nrows, dtype=np.int32)
@@ -264,10 +304,18 @@ def cpu_baseline(case: Case, target_s: float = 12.0) -> dict:
     run(rows)
     dt = time.perf_counter() - t0
     flops = 2.0 * nrows * case.N * case.K
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": o.num_threads(), "kind": "oracle",
-            "sample": f"{nrows} full output rows of {case.name} ({case.M}x{case.N}x{case.K}), "
-                      f"{flops / 1e9:.1f} GFLOP in {dt:.1f} s, fp64, OpenMP",
-            "seconds": round(dt, 2), "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "rows": nrows,
+            "seconds": round(dt, 3), "gflop": round(flops / 1e9, 2)}
+
+
+def cpu_baseline(case: Case, target_s: float = 12.0) -> dict:
+    """The oracle as it stands, on a bounded sample of whole output rows of the workload
+    (all M rows when they take less than target_s)."""
+    r = oracle_time(case, target_s)
+    return {"value": r["value"], "unit": "TFLOP/s", "cores": r["cores"], "kind": "oracle",
+            "sample": f"{r['rows']} full output rows of {case.name} ({case.M}x{case.N}x{case.K}), "
+                      f"{r['gflop']:.1f} GFLOP in {r['seconds']:.1f} s, fp64, OpenMP",
+            "seconds": r["seconds"], "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def cpu_model() -> str:
@@ -353,6 +401,15 @@ def profile_mode(name: str, steps: int, warmup: int) -> int:
         elif kind == "small_m":
             _, wl, rows = name.split(":")
             case = Case(wl, 0, stream, rows=int(rows))
+        elif name.startswith("twin:"):
+            case = Case(name[len("twin:"):], 0, stream, twin=True)
+        elif name.startswith("ksweep:"):
+            # ksweep:M,N,K -- route BS at that shape (the K sweep's points); ksweep_pt:M,N,K route PT
+            M, N, K = (int(v) for v in name.split(":")[1].split(","))
+            case = Case("ksweep", 0, stream, shape=(M, N, K))
+        elif name.startswith("ksweep_pt:"):
+            M, N, K = (int(v) for v in name.split(":")[1].split(","))
+            case = Case("ksweep", 0, stream, twin=True, shape=(M, N, K))
         else:
             case = Case(name, 0, stream)
         wall, ev = case.time_launches(steps, warmup, stream)
@@ -419,18 +476,159 @@ def ingest_counters(dirs: list[str]) -> int:
     return 0
 
 
+def _fit_line(xs, ys):
+    """Least-squares y = a + b x; returns (a, b, max abs residual)."""
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((x - mx) ** 2 for x in xs)
+    b = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sxx if sxx else 0.0
+    a = my - b * mx
+    return a, b, max(abs(y - (a + b * x)) for x, y in zip(xs, ys))
+
+
+def ksweep_mode(M: int, N: int, Ks, stream) -> int:
+    """Time against depth at a fixed output shape, routes BS and PT (the same matrix work without
+    the per-block promote), each point parity-checked before it is timed; fit
+    time = fixed + slope * (K/128) per route (page "Flydsl Fp8 Blockscale Gemm", Bottleneck
+    diagnosis: the K sweep separates a shape's fixed cost from its mainloop)."""
+    import torch
+    out = {"mode": "ksweep", "M": M, "N": N, "routes": {}}
+    for route in ("bs", "pt"):
+        pts = []
+        for K in Ks:
+            case = Case(f"ksweep_{M}x{N}", 0, stream, twin=(route == "pt"), shape=(M, N, K))
+            case.launch()
+            torch.cuda.synchronize()
+            par = sampled_parity(case, 8, 8)
+            med, n = case.repeated(stream)
+            us = min(med) * 1e6
+            pts.append(dict(K=K, k_blocks=K // 128, us=round(us, 2), us_med=round(sorted(med)[1] * 1e6, 2),
+                            tflops=round(case.flops / (us * 1e-6) / 1e12, 1), parity_passed=par["passed"],
+                            config=case.config))
+            log(f"[ksweep] {route} K={K}: {pts[-1]}")
+            case.free()
+            torch.cuda.empty_cache()
+        a, b, r = _fit_line([p["k_blocks"] for p in pts], [p["us"] for p in pts])
+        out["routes"][route] = {"points": pts, "fixed_us": round(a, 2), "us_per_k_block": round(b, 4),
+                                "max_residual_us": round(r, 2)}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+# the tiles the sweep tries: (block_m, block_n, waves_m, waves_n, stages, pingpong)
+SWEEP_TILES = [(256, 256, 2, 4, 2, 0), (256, 128, 4, 2, 3, 2), (128, 256, 2, 4, 3, 2), (128, 128, 2, 2, 3, 2)]
+
+
+def tile_sweep_mode(name: str, stream, group_ms=(1, 2, 4, 8, 16), tiles=None) -> int:
+    """Every tile order (group_m x XCD mapping) for each tile in `tiles` on one workload, through
+    the *_with_config entry. The library's own choice is checked against the oracle first; every
+    other configuration must give the same bits (all do the same per-element arithmetic)."""
+    import torch
+
+    import fp8_block_scaled_e4m3_amd as fb
+    case = Case(name, 0, stream)
+    case.launch()
+    torch.cuda.synchronize()
+    par = sampled_parity(case, 8, 8)
+    ref = case.C.clone()
+    base_med, _ = case.repeated(stream)
+    rows = [dict(config="selected", **case.config, us=round(min(base_med) * 1e6, 2))]
+    log(f"[tile-sweep] {name} selected {rows[-1]} parity {par}")
+    fn = {"bs": fb.fp8bs_gemm_with_config, "mx": fb.fp8mx_gemm_with_config, "pt": fb.fp8pt_gemm_with_config}[case.route]
+    for (bm, bn, wm, wn, st, pp) in (tiles or SWEEP_TILES):
+        if case.N % bn:
+            continue
+        for gm in group_ms:
+            for xcd in (0, 1, 2):
+                cfg = fb.Config(bm, bn, wm, wn, st, gm, xcd, 1, pp)
+                case.launch = lambda cfg=cfg: fn(case.A, case.sa, case.B, case.sb, case.C, cfg, stream)
+                case.C.fill_(0)
+                try:
+                    case.launch()
+                except fb.Fp8bsError as e:  # not instantiated for this route
+                    log(f"[tile-sweep] {cfg}: {e}")
+                    break
+                torch.cuda.synchronize()
+                same = bool(torch.equal(case.C, ref))
+                med, _ = case.repeated(stream, preroll_ms=30.0, time_s=0.02)
+                rows.append(dict(tile=f"{bm}x{bn}", waves=f"{wm}x{wn}", stages=st, pingpong=pp, group_m=gm,
+                                 xcd_remap=xcd, us=round(min(med) * 1e6, 2), bitwise_equal=same))
+                log(f"[tile-sweep] {rows[-1]}")
+    print(json.dumps({"mode": "tile_sweep", "workload": name, "parity": par, "rows": rows}), flush=True)
+    return 0
+
+
+# SQ/GRBM counters of the two per-dispatch passes, and what is derived from them
+PMC_PASSES = {
+    "a": ["GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES",
+          "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_LDS_BANK_CONFLICT"],
+    "b": ["GRBM_GUI_ACTIVE", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_LDS",
+          "SQ_LDS_IDX_ACTIVE", "SQ_ACTIVE_INST_VMEM", "SQ_INSTS_LDS", "SQ_ACTIVE_INST_ANY"],
+}
+
+
+def summarize_pmc(dirs: list[str], match: str = "gemm_kernel") -> int:
+    """Median per dispatch of every counter in the rocprofv3 counter_collection.csv files under
+    `dirs` for kernels whose name contains `match`, and the derived utilisations: MFMA busy =
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs), VALU busy = SQ_ACTIVE_INST_VALU /
+    (GRBM_GUI_ACTIVE x CUs) (the definitions rocprofv3 lists as MfmaUtil and VALUBusy), LDS
+    bank-conflict share = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE."""
+    vals: dict[str, list[float]] = {}
+    kernel = None
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if match not in r["Kernel_Name"]:
+                        continue
+                    kernel = r["Kernel_Name"]
+                    vals.setdefault((d, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
+    med = {}
+    for (d, name), v in vals.items():
+        v = sorted(v)
+        med.setdefault(name, v[len(v) // 2])
+    cus, simds = 256, 1024
+    out = {"kernel": kernel, "counters_median_per_dispatch": med}
+    g = med.get("GRBM_GUI_ACTIVE")
+    if g:
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+            out["mfma_busy"] = round(med["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * simds), 4)
+        if "SQ_ACTIVE_INST_VALU" in med:
+            out["valu_busy"] = round(med["SQ_ACTIVE_INST_VALU"] / (g * cus), 4)
+    if med.get("SQ_LDS_IDX_ACTIVE"):
+        out["lds_bank_conflict_share"] = round(med.get("SQ_LDS_BANK_CONFLICT", 0.0) / med["SQ_LDS_IDX_ACTIVE"], 5)
+    if med.get("SQ_INSTS_MFMA"):
+        out["valu_insts_per_mfma"] = round(med.get("SQ_INSTS_VALU", 0.0) / med["SQ_INSTS_MFMA"], 3)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=400)
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--preroll-ms", type=float, default=100.0,
+                    help="milliseconds of untimed launches before the counted warmup (clock ramp)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle timings")
     ap.add_argument("--only", default=None, help="time only this workload (plus the main one)")
     ap.add_argument("--profile", default=None, help="rocprofv3 driver mode for one workload")
     ap.add_argument("--ingest-counters", nargs="+", default=None)
+    ap.add_argument("--ksweep", action="store_true")
+    ap.add_argument("--ksweep-shape", default="4096,2048")
+    ap.add_argument("--ksweep-k", default="1024,2048,3584,7168")
+    ap.add_argument("--tile-sweep", default=None)
+    ap.add_argument("--summarize-pmc", nargs="+", default=None,
+                    help="rocprofv3 --pmc output dirs -> median counters and utilisations (JSON)")
+    ap.add_argument("--pmc-pass", default=None, help="print the counters of pass a or b (for --pmc)")
     args = ap.parse_args()
     if args.ingest_counters:
         return ingest_counters(args.ingest_counters)
+    if args.summarize_pmc:
+        return summarize_pmc(args.summarize_pmc)
+    if args.pmc_pass:
+        print(" ".join(PMC_PASSES[args.pmc_pass]))
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library is a single-GPU kernel and no "
               "multi-GPU path exists (run with --gpus 1).", file=sys.stderr)
@@ -444,140 +642,102 @@ def main() -> int:
         return 2
     if args.profile:
         return profile_mode(args.profile, args.steps, args.warmup)
-    props = torch.cuda.get_device_properties(0)
     stream = torch.cuda.Stream()
-    per_shape = {}
+    if args.ksweep:
+        M, N = (int(v) for v in args.ksweep_shape.split(","))
+        with torch.cuda.stream(stream):
+            return ksweep_mode(M, N, [int(k) for k in args.ksweep_k.split(",")], stream)
+    if args.tile_sweep:
+        with torch.cuda.stream(stream):
+            return tile_sweep_mode(args.tile_sweep, stream)
+    props = torch.cuda.get_device_properties(0)
     names = [MAIN] + [n for n in workload.CONFIGS if n != MAIN]
     if args.only:
         names = [MAIN] + ([args.only] if args.only != MAIN else [])
-    main_row = None
+    per_config, oracle_rates, twin = {}, {}, {}
     with torch.cuda.stream(stream):
-        scratch = torch.empty(COLD_SCRATCH_BYTES, dtype=torch.uint8, device="cuda:0")
+        # cold launches follow a read of 1 GiB (more than the 8 x 4 MB of L2 and the 256 MB
+        # MALL): the operands are evicted and no dirty lines are left to write back
+        evict_buf = torch.ones(COLD_SCRATCH_BYTES // 4, dtype=torch.int32, device="cuda:0")
+        evict = lambda: evict_buf.amax()
+
+        # ---- the main workload: parity first, then the pre-roll, the warmup and the counted steps
+        main = Case(MAIN, 0, stream)
+        main.launch()
+        torch.cuda.synchronize()
+        main_parity = sampled_parity(main, 16, 16)
+        log(f"[bench] parity {MAIN} {main_parity}")
+        main_out = main.C.clone()
+        t_pre = time.perf_counter()
+        preroll_n = main.preroll(args.preroll_ms)
+        preroll_ms = (time.perf_counter() - t_pre) * 1e3
+        wall, ev = main.time_launches(args.steps, args.warmup, stream)
+        main_same = bool(torch.equal(main.C, main_out))
+        log(f"[bench] {MAIN}: {args.steps} steps after {preroll_n} pre-roll launches ({preroll_ms:.0f} ms) and "
+            f"{args.warmup} warmup: wall {wall * 1e6:.2f} us, events {ev * 1e6:.2f} us per launch")
+
+        # ---- every workload: parity, then min of 3 medians, then cold launches
+        baseline, ceiling = None, None
         for name in names:
-            case = Case(name, 0, stream)
+            case = main if name == MAIN else Case(name, 0, stream)
             if name == MAIN:
-                wall, ev = case.time_launches(args.steps, args.warmup, stream)
-                steps = args.steps
+                par = main_parity
             else:
-                wall, ev, steps = case.steady_state(stream)
-            tflops = case.flops / ev / 1e12
+                case.launch()
+                torch.cuda.synchronize()
+                par = sampled_parity(case, 8, 8)
+            out = case.C.clone()
+            med, n = case.repeated(stream)
+            same = bool(torch.equal(case.C, out))
+            cold_med, cold_min = case.cold(stream, evict)
+            us = min(med)
             nbytes = algorithmic_bytes(case.route, case.M, case.N, case.K)
-            row = dict(M=case.M, N=case.N, K=case.K, route=case.route, us=round(ev * 1e6, 2),
-                       tflops=round(tflops, 1), pct_peak=round(100 * tflops / PEAK_FP8_TFLOPS, 2),
-                       hbm_gbs_algorithmic=round(nbytes / ev / 1e9, 1), timed_launches=steps,
-                       config=case.config)
-            cold_med, cold_min = case.cold(stream, scratch)
-            row.update(cold_us=round(cold_med * 1e6, 2), cold_min_us=round(cold_min * 1e6, 2),
-                       cold_tflops=round(case.flops / cold_med / 1e12, 1))
-            log(f"[bench] {name}: {row}")
-            # the timed output against the oracle on sampled whole rows and columns
-            row["parity"] = sampled_parity(case, *((16, 16) if name == MAIN else (8, 8)))
-            log(f"[bench] parity {name} {row['parity']}")
+            per_config[name] = dict(
+                shape=f"{case.M}x{case.N}x{case.K}", route=case.route, us=round(us * 1e6, 2),
+                us_med=round(sorted(med)[1] * 1e6, 2), tflops=round(case.flops / us / 1e12, 1),
+                frac=round(case.flops / us / 1e12 / PEAK_FP8_TFLOPS, 4),
+                frac_hbm=round(nbytes / us / 1e9 / PEAK_HBM_GBS, 4), cold_us=round(cold_med * 1e6, 2),
+                parity_passed=bool(par["passed"] and same))
+            log(f"[bench] {name}: {per_config[name]} launches/run {n} medians_us "
+                f"{[round(m * 1e6, 2) for m in med]} cold_min_us {cold_min * 1e6:.2f} config {case.config} "
+                f"parity {par} bitwise_repeatable {same}")
+            if not args.no_cpu:
+                oracle_rates[name] = oracle_time(case, 1.0)
+                log(f"[bench] oracle {name}: {oracle_rates[name]}")
             if name == MAIN:
                 ceiling = mfma_ceiling(case, stream)
                 log(f"[bench] mfma ceiling {ceiling}")
-                baseline = None if args.no_cpu else cpu_baseline(case)
-                if baseline:
+                if not args.no_cpu:
+                    baseline = cpu_baseline(case)
                     log(f"[bench] cpu baseline {baseline}")
-                main_row = dict(wall=wall, ev=ev, case=case, nbytes=nbytes, baseline=baseline, ceiling=ceiling)
-            else:
+            if case is not main:
                 case.free()
                 del case
                 torch.cuda.empty_cache()
-            per_shape[name] = row
 
-        # the promote-free twin (route PT) on the route-BS shapes: same matrix work, scales
-        # applied once in the epilogue -- the cost of the per-block promote is the difference
-        twin = {}
+        # ---- the promote-free twin (route PT) on the route-BS shapes: the same matrix work with
+        # the scales applied once in the epilogue; BS / PT is the cost of the per-block promote
         for name in [n for n in names if workload.CONFIGS[n]["route"] == "bs" and n != "tiny"]:
             tc = Case(name, 0, stream, twin=True)
-            _, ev, steps = tc.steady_state(stream)
-            bs_us = per_shape[name]["us"]
-            twin[name] = dict(us=round(ev * 1e6, 2), tflops=round(tc.flops / ev / 1e12, 1),
-                              pct_peak=round(100 * tc.flops / ev / 1e12 / PEAK_FP8_TFLOPS, 2),
-                              bs_over_twin=round(bs_us / (ev * 1e6), 3), config=tc.config,
-                              parity=sampled_parity(tc, 8, 8))
-            log(f"[bench] twin {name}: {twin[name]}")
+            tc.launch()
+            torch.cuda.synchronize()
+            par = sampled_parity(tc, 8, 8)
+            med, _ = tc.repeated(stream)
+            us = min(med) * 1e6
+            twin[name] = dict(us=round(us, 2), frac=round(tc.flops / us / 1e6 / PEAK_FP8_TFLOPS, 4),
+                              bs_over_twin=round(per_config[name]["us"] / us, 3), parity_passed=par["passed"])
+            log(f"[bench] twin {name}: {twin[name]} config {tc.config} parity {par}")
             tc.free()
             del tc
             torch.cuda.empty_cache()
 
-        # the activation quantisers (bf16 activations -> e4m3 codes + the GEMM's scale layout):
-        # memory-bound, measured against HBM bandwidth on each route's activation shape
-        quant = {}
-        import fp8_block_scaled_e4m3_amd as fb
-        for qname, qroute in (("narrow_n", "bs"), ("k_light", "bs"), ("mxfp8", "mx")):
-            cfgq = workload.CONFIGS[qname]
-            Mq, Kq = cfgq["M"], cfgq["K"]
-            xq = torch.randn((Mq, Kq), dtype=torch.float32, device="cuda:0").to(torch.bfloat16)
-            Aq = torch.empty((Mq, Kq), dtype=torch.uint8, device="cuda:0")
-            if qroute == "bs":
-                Sq = torch.empty((Kq // 128, Mq), dtype=torch.float32, device="cuda:0")
-                qlaunch = lambda: fb.fp8bs_quantize_act(xq, Aq, Sq, stream)
-                qbytes = Mq * Kq * 3 + Mq * (Kq // 128) * 4
-            else:
-                Sq = torch.empty((Mq, Kq // 32), dtype=torch.uint8, device="cuda:0")
-                qlaunch = lambda: fb.fp8mx_quantize_act(xq, Aq, Sq, stream)
-                qbytes = Mq * Kq * 3 + Mq * (Kq // 32)
-            for _ in range(200):
-                qlaunch()
-            torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(200):
-                qlaunch()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            qt = e0.elapsed_time(e1) / 1e3 / 200
-            quant[f"{qroute}_{Mq}x{Kq}_bf16"] = dict(us=round(qt * 1e6, 2), bytes=qbytes,
-                                                    gbs=round(qbytes / qt / 1e9, 1),
-                                                    frac_hbm=round(qbytes / qt / 1e9 / PEAK_HBM_GBS, 3))
-            log(f"[bench] quantiser {qroute} {Mq}x{Kq}: {quant[f'{qroute}_{Mq}x{Kq}_bf16']}")
-            del xq, Aq, Sq
+        quant = quantiser_rows(stream) if not args.only else {}
+        small = small_m_rows(stream, evict) if not args.only else {}
 
-        # few rows (the decode regime): the weights dominate the traffic, so the bound is HBM.
-        # Hot = back-to-back launches (weights may stay in the MALL between launches), cold =
-        # single launches after a 1 GiB write. `us` is the plain entry point (the kernel the
-        # library selects); for route BS the small-M kernel and the main kernel (with the 128-row
-        # tile the library uses when M <= 128) are each timed beside it.
-        small = {}
-        for wname in ("narrow_n", "k_light", "narrow_n_16k", "wide_n", "mxfp8"):
-            for rows in (1, 16, 64):
-                dc = Case(wname, 0, stream, rows=rows)
-                _, ev, _ = dc.steady_state(stream, 0.03, 0.03)
-                cold_med, _ = dc.cold(stream, scratch, reps=9)
-                nb = algorithmic_bytes(dc.route, dc.M, dc.N, dc.K)
-                row = dict(M=dc.M, N=dc.N, K=dc.K, route=dc.route, small_m=dc.config.get("small_m", 0),
-                           us=round(ev * 1e6, 2), cold_us=round(cold_med * 1e6, 2), bytes=nb,
-                           cold_gbs=round(nb / cold_med / 1e9, 1),
-                           cold_frac_hbm=round(nb / cold_med / 1e9 / PEAK_HBM_GBS, 3))
-                torch.cuda.synchronize()  # the selected kernel's output, checked against the oracle
-                row["parity"] = sampled_parity(dc, min(rows, 8), 8)
-                if dc.route == "bs":
-                    forced = fb.Config()
-                    forced.small_m = 1
-                    # the main kernel's tile for one row of 128-row tiles, as the selector takes it:
-                    # 128x256 where those fill the CUs or need fewer rounds of them than 128x128,
-                    # else 128x128 (both warp-specialised)
-                    wide = dc.N % 256 == 0 and (dc.N // 256 >= 256 or -(-dc.N // 256 // 256) < -(-dc.N // 128 // 256))
-                    main_cfg = fb.Config(128, 256, 2, 4, 3, 4, 1, 1, 2) if wide else fb.Config(128, 128, 2, 2, 3, 4, 1, 1, 2)
-                    for key, c in (("small_m_kernel", forced), ("main_kernel", main_cfg)):
-                        dc.launch = lambda dc=dc, c=c: fb.fp8bs_gemm_with_config(
-                            dc.A, dc.sa, dc.B, dc.sb, dc.C, c, stream)
-                        _, evm, _ = dc.steady_state(stream, 0.03, 0.03)
-                        cold_m, _ = dc.cold(stream, scratch, reps=9)
-                        row.update({f"{key}_us": round(evm * 1e6, 2), f"{key}_cold_us": round(cold_m * 1e6, 2)})
-                    row["main_kernel_tile"] = f"{main_cfg.block_m}x{main_cfg.block_n}"
-                small[f"{wname}_weights_M{rows}"] = row
-                log(f"[bench] small-M {wname} M={rows}: {row}")
-                dc.free()
-                del dc
-            torch.cuda.empty_cache()
-
-    case = main_row["case"]
-    value = case.flops / main_row["wall"] / 1e12
-    achieved = case.flops / main_row["ev"] / 1e12
+    value = main.flops / wall / 1e12
+    achieved = main.flops / ev / 1e12
+    parities = [r["parity_passed"] for r in per_config.values()] + [r["parity_passed"] for r in twin.values()] + \
+        [r["parity_passed"] for r in small.values()] + [main_parity["passed"], main_same]
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -585,33 +745,119 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(main_row["wall"] * 1e3, 5),
+        "ms_per_step": round(wall * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8e4m3",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, quantised on the host)",
-        "config": {"workload": f"{MAIN} blockscale GEMM M={case.M} N={case.N} K={case.K} "
+        "config": {"workload": f"{MAIN} blockscale GEMM M={main.M} N={main.N} K={main.K} "
                                "(fp32 1x128 / 128x128 scales, bf16 out)",
-                   "M": case.M, "N": case.N, "K": case.K, "route": "bs"},
+                   "M": main.M, "N": main.N, "K": main.K, "route": "bs"},
+        "preroll_ms": round(preroll_ms, 1),
+        "parity_all_passed": all(parities),
+        "per_config": per_config,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP8_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
-                     "traffic": committed_traffic(MAIN),
-                     "kernel": "gemm_kernel (route BS)", "avg_launch_us": round(main_row["ev"] * 1e6, 2),
-                     "flop_per_launch": case.flops, "algorithmic_bytes": main_row["nbytes"]},
-        "mfma_ceiling": main_row["ceiling"],
-        "cpu_baseline": main_row["baseline"],
-        "per_shape": per_shape,
-        "ceiling_twin": twin,
+                     "traffic": committed_traffic(MAIN), "kernel": "gemm_kernel (route BS)",
+                     "avg_launch_us": round(ev * 1e6, 2), "flop_per_launch": main.flops,
+                     "algorithmic_bytes": algorithmic_bytes("bs", main.M, main.N, main.K)},
+        "cpu_baseline": baseline,
+        "oracle": {n: {"tflops": round(r["value"], 4), "rows": r["rows"], "s": r["seconds"]}
+                   for n, r in oracle_rates.items()},
+        "oracle_note": "fp64 OpenMP oracle on the first `rows` whole output rows of each workload (a sample)",
+        "twin": twin,
+        "mfma_ceiling": ceiling,
         "quantiser": quant,
-        "small_m": small,
-        "parity_all_passed": all(r["parity"]["passed"] for r in
-                                 list(per_shape.values()) + list(twin.values()) + list(small.values())),
+        "small_m": {k: {"us": r["us"], "cold_us": r["cold_us"], "cold_frac_hbm": r["cold_frac_hbm"],
+                        "parity_passed": r["parity_passed"]} for k, r in small.items()},
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "kernel_source_sha256": kernel_source_hash()[:16]},
     }
-    print(json.dumps(out), flush=True)
+    print(json.dumps(out, separators=(",", ":")), flush=True)
     return 0
+
+
+def quantiser_rows(stream) -> dict:
+    """The activation quantisers (bf16 activations -> e4m3 codes + the GEMM's scale layout):
+    memory-bound, timed against the HBM peak on each route's activation shape."""
+    import torch
+
+    import fp8_block_scaled_e4m3_amd as fb
+    import workload
+    quant = {}
+    for qname, qroute in (("narrow_n", "bs"), ("k_light", "bs"), ("mxfp8", "mx")):
+        cfgq = workload.CONFIGS[qname]
+        Mq, Kq = cfgq["M"], cfgq["K"]
+        xq = torch.randn((Mq, Kq), dtype=torch.float32, device="cuda:0").to(torch.bfloat16)
+        Aq = torch.empty((Mq, Kq), dtype=torch.uint8, device="cuda:0")
+        if qroute == "bs":
+            Sq = torch.empty((Kq // 128, Mq), dtype=torch.float32, device="cuda:0")
+            qlaunch = lambda: fb.fp8bs_quantize_act(xq, Aq, Sq, stream)
+            qbytes = Mq * Kq * 3 + Mq * (Kq // 128) * 4
+        else:
+            Sq = torch.empty((Mq, Kq // 32), dtype=torch.uint8, device="cuda:0")
+            qlaunch = lambda: fb.fp8mx_quantize_act(xq, Aq, Sq, stream)
+            qbytes = Mq * Kq * 3 + Mq * (Kq // 32)
+        for _ in range(200):
+            qlaunch()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(200):
+            qlaunch()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        qt = e0.elapsed_time(e1) / 1e3 / 200
+        key = f"{qroute}_{Mq}x{Kq}_bf16"
+        quant[key] = dict(us=round(qt * 1e6, 2), frac_hbm=round(qbytes / qt / 1e9 / PEAK_HBM_GBS, 3))
+        log(f"[bench] quantiser {key}: {quant[key]} bytes {qbytes} GB/s {qbytes / qt / 1e9:.1f}")
+        del xq, Aq, Sq
+    return quant
+
+
+def small_m_rows(stream, evict) -> dict:
+    """Few rows (the decode regime): the weights dominate the traffic, so the bound is HBM. Hot =
+    back-to-back launches, cold = single launches after the eviction read. `us` is the plain
+    entry point (the kernel the library selects); for route BS the small-M kernel and the main
+    kernel (the 128-row tile the library uses when M <= 128) are each timed beside it, on stderr."""
+    import torch
+
+    import fp8_block_scaled_e4m3_amd as fb
+    small = {}
+    for wname in ("narrow_n", "k_light", "narrow_n_16k", "wide_n", "mxfp8"):
+        for rows in (1, 16, 64):
+            dc = Case(wname, 0, stream, rows=rows)
+            dc.launch()
+            torch.cuda.synchronize()
+            par = sampled_parity(dc, min(rows, 8), 8)
+            med, _ = dc.repeated(stream, preroll_ms=30.0, time_s=0.02)
+            cold_med, _ = dc.cold(stream, evict, reps=9)
+            nb = algorithmic_bytes(dc.route, dc.M, dc.N, dc.K)
+            row = dict(M=dc.M, N=dc.N, K=dc.K, route=dc.route, small_m=dc.config.get("small_m", 0),
+                       us=round(min(med) * 1e6, 2), cold_us=round(cold_med * 1e6, 2), bytes=nb,
+                       cold_frac_hbm=round(nb / cold_med / 1e9 / PEAK_HBM_GBS, 3), parity_passed=par["passed"])
+            if dc.route == "bs":
+                forced = fb.Config()
+                forced.small_m = 1
+                # the main kernel's tile for one row of 128-row tiles, as the selector takes it:
+                # 128x256 where those fill the CUs or need fewer rounds of them than 128x128,
+                # else 128x128 (both warp-specialised)
+                wide = dc.N % 256 == 0 and (dc.N // 256 >= 256 or -(-dc.N // 256 // 256) < -(-dc.N // 128 // 256))
+                main_cfg = fb.Config(128, 256, 2, 4, 3, 4, 1, 1, 2) if wide else fb.Config(128, 128, 2, 2, 3, 4, 1, 1, 2)
+                for key, c in (("small_m_kernel", forced), ("main_kernel", main_cfg)):
+                    dc.launch = lambda dc=dc, c=c: fb.fp8bs_gemm_with_config(dc.A, dc.sa, dc.B, dc.sb, dc.C, c, stream)
+                    medm, _ = dc.repeated(stream, preroll_ms=30.0, time_s=0.02)
+                    cold_m, _ = dc.cold(stream, evict, reps=9)
+                    row.update({f"{key}_us": round(min(medm) * 1e6, 2), f"{key}_cold_us": round(cold_m * 1e6, 2)})
+                row["main_kernel_tile"] = f"{main_cfg.block_m}x{main_cfg.block_n}"
+            small[f"{wname}_M{rows}"] = row
+            log(f"[bench] small-M {wname} M={rows}: {row} parity {par}")
+            dc.free()
+            del dc
+        torch.cuda.empty_cache()
+    return small
 
 
 if __name__ == "__main__":

@@ -23,8 +23,8 @@ import torch
 
 __all__ = [
     "LIBRARY", "Fp8bsError", "lib", "fp8bs_version", "fp8bs_strerror",
-    "fp8bs_prep_weight_bytes", "fp8bs_prep_weights", "fp8bs_gemm",
-    "fp8mx_packed_scale_bytes", "fp8mx_pack_a_scale", "fp8mx_prep_weights", "fp8mx_gemm",
+    "fp8bs_prep_weight_bytes", "fp8bs_prep_bytes", "fp8bs_prep_weights", "fp8bs_gemm",
+    "fp8mx_packed_scale_bytes", "fp8mx_scale_bytes", "fp8mx_pack_a_scale", "fp8mx_prep_weights", "fp8mx_gemm",
     "prep_weights", "mx_prep_weights", "mx_pack_a_scale",
     "Config", "ROUTE_BS", "ROUTE_MX", "fp8bs_select_config", "fp8bs_gemm_with_config", "fp8mx_gemm_with_config",
     "fp8bs_mfma_ceiling", "ROUTE_PT", "fp8pt_gemm", "fp8pt_gemm_with_config",
@@ -41,9 +41,11 @@ SIGNATURES = {
     "fp8bs_version": (_int, []),
     "fp8bs_strerror": (ctypes.c_char_p, [_int]),
     "fp8bs_prep_weight_bytes": (_size, [_int, _int]),
+    "fp8bs_prep_bytes": (_size, [_int, _int]),
     "fp8bs_prep_weights": (_int, [_vp, _vp, _int, _int, _vp]),
     "fp8bs_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp]),
     "fp8mx_packed_scale_bytes": (_size, [_int, _int]),
+    "fp8mx_scale_bytes": (_size, [_int, _int]),
     "fp8mx_pack_a_scale": (_int, [_vp, _vp, _int, _int, _vp]),
     "fp8mx_prep_weights": (_int, [_vp, _vp, _vp, _vp, _int, _int, _vp]),
     "fp8mx_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp]),
@@ -110,6 +112,63 @@ def _ptr(t: torch.Tensor | None) -> int | None:
     return t.data_ptr()
 
 
+# fp8 e4m3 codes may come as raw bytes or as torch's own e4m3 type (same bytes)
+_CODE_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _expect(fn: str, arg: str, t: torch.Tensor, dtypes, shape=None, numel=None) -> None:
+    """Raise ValueError unless t has one of `dtypes` and exactly `shape` (or `numel` elements,
+    for the opaque prepared buffers). Checked before anything reaches the library, so a buffer
+    of the wrong size or layout never becomes an out-of-bounds access on the device."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{fn}: {arg} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{fn}: {arg} has dtype {t.dtype}, expected {' or '.join(map(str, dtypes))}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{fn}: {arg} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{fn}: {arg} has {t.numel()} elements, expected {numel}")
+
+
+def _matrix(fn: str, arg: str, t: torch.Tensor, dtypes) -> tuple[int, int]:
+    if not isinstance(t, torch.Tensor) or t.dim() != 2:
+        raise ValueError(f"{fn}: {arg} must be a 2-D tensor")
+    _expect(fn, arg, t, dtypes)
+    return tuple(t.shape)
+
+
+def _same_device(fn: str, *ts) -> None:
+    devs = {t.device for t in ts if t is not None}
+    if len(devs) > 1:
+        raise ValueError(f"{fn}: tensors are on different devices {sorted(map(str, devs))}")
+
+
+def _gemm_operands(fn: str, route: str, A, a_scale, B_prep, b_scale, C, packed_a: bool = True):
+    """(M, N, K) after checking every operand of a GEMM entry point against A [M, K] and C [M, N]."""
+    M, K = _matrix(fn, "A", A, _CODE_DTYPES)
+    Mc, N = _matrix(fn, "C", C, (torch.bfloat16,))
+    if Mc != M:
+        raise ValueError(f"{fn}: C has {Mc} rows, A has {M}")
+    _expect(fn, "B_prep", B_prep, _CODE_DTYPES, numel=N * K)
+    # a shape the route rejects never reaches a kernel: the library returns FP8BS_E_SHAPE for it,
+    # so the scale buffers are sized only for shapes it accepts
+    if route == "bs":
+        if K % 128 == 0 and N % 128 == 0:
+            _expect(fn, "a_scale", a_scale, (torch.float32,), shape=(K // 128, M))
+            _expect(fn, "b_scale", b_scale, (torch.float32,), shape=(N // 128, K // 128))
+    elif route == "pt":
+        _expect(fn, "a_scale", a_scale, (torch.float32,), shape=(M,))
+        _expect(fn, "b_scale", b_scale, (torch.float32,), shape=(N,))
+    elif K % 32 == 0:
+        if packed_a:
+            _expect(fn, "a_scale_packed", a_scale, (torch.uint8,), numel=M * (K // 32))
+        else:
+            _expect(fn, "a_e8m0", a_scale, (torch.uint8,), shape=(M, K // 32))
+        _expect(fn, "b_scale_packed", b_scale, (torch.uint8,), numel=N * (K // 32))
+    _same_device(fn, A, a_scale, B_prep, b_scale, C)
+    return M, N, K
+
+
 def _stream(stream) -> int | None:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -139,8 +198,18 @@ def fp8mx_packed_scale_bytes(rows: int, K: int) -> int:
     return lib.fp8mx_packed_scale_bytes(rows, K)
 
 
+def fp8bs_prep_bytes(N: int, K: int) -> int:
+    return lib.fp8bs_prep_bytes(N, K)
+
+
+def fp8mx_scale_bytes(rows: int, K: int) -> int:
+    return lib.fp8mx_scale_bytes(rows, K)
+
+
 def fp8bs_prep_weights(B: torch.Tensor, B_prep: torch.Tensor, stream=None) -> None:
-    N, K = B.shape
+    N, K = _matrix("fp8bs_prep_weights", "B", B, _CODE_DTYPES)
+    _expect("fp8bs_prep_weights", "B_prep", B_prep, _CODE_DTYPES, numel=N * K)
+    _same_device("fp8bs_prep_weights", B, B_prep)
     _check("fp8bs_prep_weights", lib.fp8bs_prep_weights(_ptr(B), _ptr(B_prep), N, K, _stream(stream)))
 
 
@@ -148,30 +217,37 @@ def fp8bs_gemm(A: torch.Tensor, a_scale: torch.Tensor, B_prep: torch.Tensor, b_s
                C: torch.Tensor, stream=None) -> torch.Tensor:
     """C[M,N] (bf16) from A [M,K] (uint8 e4m3 codes), a_scale [K/128, M] fp32, B_prep from
     fp8bs_prep_weights of B [N,K], b_scale [N/128, K/128] fp32."""
-    M, K = A.shape
-    N = C.shape[1]
+    M, N, K = _gemm_operands("fp8bs_gemm", "bs", A, a_scale, B_prep, b_scale, C)
     _check("fp8bs_gemm", lib.fp8bs_gemm(_ptr(A), _ptr(a_scale), _ptr(B_prep), _ptr(b_scale), _ptr(C),
                                         M, N, K, _stream(stream)))
     return C
 
 
 def fp8mx_pack_a_scale(a_e8m0: torch.Tensor, a_scale_packed: torch.Tensor, stream=None) -> None:
-    M, G = a_e8m0.shape
+    M, G = _matrix("fp8mx_pack_a_scale", "a_e8m0", a_e8m0, (torch.uint8,))
+    _expect("fp8mx_pack_a_scale", "a_scale_packed", a_scale_packed, (torch.uint8,), numel=M * G)
+    _same_device("fp8mx_pack_a_scale", a_e8m0, a_scale_packed)
     _check("fp8mx_pack_a_scale", lib.fp8mx_pack_a_scale(_ptr(a_e8m0), _ptr(a_scale_packed), M, G * 32,
                                                         _stream(stream)))
 
 
 def fp8mx_prep_weights(B: torch.Tensor, b_e8m0: torch.Tensor, B_prep: torch.Tensor,
                        b_scale_packed: torch.Tensor, stream=None) -> None:
-    N, K = B.shape
+    fn = "fp8mx_prep_weights"
+    N, K = _matrix(fn, "B", B, _CODE_DTYPES)
+    if K % 32:
+        raise ValueError(f"{fn}: K ({K}) must be a multiple of 32")
+    _expect(fn, "b_e8m0", b_e8m0, (torch.uint8,), shape=(N, K // 32))
+    _expect(fn, "B_prep", B_prep, _CODE_DTYPES, numel=N * K)
+    _expect(fn, "b_scale_packed", b_scale_packed, (torch.uint8,), numel=N * (K // 32))
+    _same_device(fn, B, b_e8m0, B_prep, b_scale_packed)
     _check("fp8mx_prep_weights", lib.fp8mx_prep_weights(_ptr(B), _ptr(b_e8m0), _ptr(B_prep),
                                                         _ptr(b_scale_packed), N, K, _stream(stream)))
 
 
 def fp8mx_gemm(A: torch.Tensor, a_scale_packed: torch.Tensor, B_prep: torch.Tensor,
                b_scale_packed: torch.Tensor, C: torch.Tensor, stream=None) -> torch.Tensor:
-    M, K = A.shape
-    N = C.shape[1]
+    M, N, K = _gemm_operands("fp8mx_gemm", "mx", A, a_scale_packed, B_prep, b_scale_packed, C)
     _check("fp8mx_gemm", lib.fp8mx_gemm(_ptr(A), _ptr(a_scale_packed), _ptr(B_prep), _ptr(b_scale_packed),
                                         _ptr(C), M, N, K, _stream(stream)))
     return C
@@ -181,16 +257,14 @@ def fp8pt_gemm(A: torch.Tensor, a_scale: torch.Tensor, B_prep: torch.Tensor, b_s
                C: torch.Tensor, stream=None) -> torch.Tensor:
     """Route PT (promote-free twin): C[M,N] (bf16) = a_scale[m] * b_scale[n] * (A B^T)[m,n] with
     A [M,K] uint8 e4m3 codes, a_scale [M] fp32, B_prep from fp8bs_prep_weights, b_scale [N] fp32."""
-    M, K = A.shape
-    N = C.shape[1]
+    M, N, K = _gemm_operands("fp8pt_gemm", "pt", A, a_scale, B_prep, b_scale, C)
     _check("fp8pt_gemm", lib.fp8pt_gemm(_ptr(A), _ptr(a_scale), _ptr(B_prep), _ptr(b_scale), _ptr(C),
                                         M, N, K, _stream(stream)))
     return C
 
 
 def fp8pt_gemm_with_config(A, a_scale, B_prep, b_scale, C, config: Config, stream=None):
-    M, K = A.shape
-    N = C.shape[1]
+    M, N, K = _gemm_operands("fp8pt_gemm_with_config", "pt", A, a_scale, B_prep, b_scale, C)
     _check("fp8pt_gemm_with_config",
            lib.fp8pt_gemm_with_config(_ptr(A), _ptr(a_scale), _ptr(B_prep), _ptr(b_scale), _ptr(C), M, N, K,
                                       ctypes.byref(config), _stream(stream)))
@@ -199,14 +273,26 @@ def fp8pt_gemm_with_config(A, a_scale, B_prep, b_scale, C, config: Config, strea
 
 def fp8bs_quantize_act(x: torch.Tensor, A_codes: torch.Tensor, a_scale: torch.Tensor, stream=None) -> None:
     """x [M,K] bf16/fp32 -> A_codes [M,K] uint8 e4m3, a_scale [K/128, M] fp32 (route BS)."""
-    M, K = x.shape
+    fn = "fp8bs_quantize_act"
+    M, K = _matrix(fn, "x", x, tuple(_IN_DTYPE))
+    if K % 128:
+        raise ValueError(f"{fn}: K ({K}) must be a multiple of 128")
+    _expect(fn, "A_codes", A_codes, _CODE_DTYPES, shape=(M, K))
+    _expect(fn, "a_scale", a_scale, (torch.float32,), shape=(K // 128, M))
+    _same_device(fn, x, A_codes, a_scale)
     _check("fp8bs_quantize_act", lib.fp8bs_quantize_act(_ptr(x), _IN_DTYPE.get(x.dtype, -1), _ptr(A_codes),
                                                         _ptr(a_scale), M, K, _stream(stream)))
 
 
 def fp8mx_quantize_act(x: torch.Tensor, A_codes: torch.Tensor, a_e8m0: torch.Tensor, stream=None) -> None:
     """x [M,K] bf16/fp32 -> A_codes [M,K] uint8 e4m3, a_e8m0 [M, K/32] uint8 (route MX)."""
-    M, K = x.shape
+    fn = "fp8mx_quantize_act"
+    M, K = _matrix(fn, "x", x, tuple(_IN_DTYPE))
+    if K % 32:
+        raise ValueError(f"{fn}: K ({K}) must be a multiple of 32")
+    _expect(fn, "A_codes", A_codes, _CODE_DTYPES, shape=(M, K))
+    _expect(fn, "a_e8m0", a_e8m0, (torch.uint8,), shape=(M, K // 32))
+    _same_device(fn, x, A_codes, a_e8m0)
     _check("fp8mx_quantize_act", lib.fp8mx_quantize_act(_ptr(x), _IN_DTYPE.get(x.dtype, -1), _ptr(A_codes),
                                                         _ptr(a_e8m0), M, K, _stream(stream)))
 
@@ -215,8 +301,7 @@ def fp8mx_gemm_small_m(A: torch.Tensor, a_e8m0: torch.Tensor, B_prep: torch.Tens
                        C: torch.Tensor, stream=None) -> torch.Tensor:
     """Route MX through the small-M kernel (meant for few rows; any M): a_e8m0 [M, K/32] uint8
     row-major (not packed)."""
-    M, K = A.shape
-    N = C.shape[1]
+    M, N, K = _gemm_operands("fp8mx_gemm_small_m", "mx", A, a_e8m0, B_prep, b_scale_packed, C, packed_a=False)
     _check("fp8mx_gemm_small_m", lib.fp8mx_gemm_small_m(_ptr(A), _ptr(a_e8m0), _ptr(B_prep), _ptr(b_scale_packed),
                                                         _ptr(C), M, N, K, _stream(stream)))
     return C
@@ -229,8 +314,7 @@ def fp8bs_select_config(route: int, M: int, N: int, K: int) -> Config:
 
 
 def fp8bs_gemm_with_config(A, a_scale, B_prep, b_scale, C, config: Config, stream=None):
-    M, K = A.shape
-    N = C.shape[1]
+    M, N, K = _gemm_operands("fp8bs_gemm_with_config", "bs", A, a_scale, B_prep, b_scale, C)
     _check("fp8bs_gemm_with_config",
            lib.fp8bs_gemm_with_config(_ptr(A), _ptr(a_scale), _ptr(B_prep), _ptr(b_scale), _ptr(C), M, N, K,
                                       ctypes.byref(config), _stream(stream)))
@@ -238,8 +322,7 @@ def fp8bs_gemm_with_config(A, a_scale, B_prep, b_scale, C, config: Config, strea
 
 
 def fp8mx_gemm_with_config(A, a_scale_packed, B_prep, b_scale_packed, C, config: Config, stream=None):
-    M, K = A.shape
-    N = C.shape[1]
+    M, N, K = _gemm_operands("fp8mx_gemm_with_config", "mx", A, a_scale_packed, B_prep, b_scale_packed, C)
     _check("fp8mx_gemm_with_config",
            lib.fp8mx_gemm_with_config(_ptr(A), _ptr(a_scale_packed), _ptr(B_prep), _ptr(b_scale_packed), _ptr(C),
                                       M, N, K, ctypes.byref(config), _stream(stream)))
@@ -250,7 +333,13 @@ def fp8bs_mfma_ceiling(A: torch.Tensor, B_prep: torch.Tensor, N: int, iters: int
                        stream=None) -> int:
     """Launch the matrix-core ceiling probe on A [M,K] and prepared weights of N rows; returns the
     FLOP count of the launch (time it with events on the stream)."""
-    M, K = A.shape
+    fn = "fp8bs_mfma_ceiling"
+    M, K = _matrix(fn, "A", A, _CODE_DTYPES)
+    _expect(fn, "B_prep", B_prep, _CODE_DTYPES)
+    if B_prep.numel() < N * K:
+        raise ValueError(f"{fn}: B_prep holds {B_prep.numel()} bytes, {N} weight rows need {N * K}")
+    _expect(fn, "sink", sink, (torch.float32,))
+    _same_device(fn, A, B_prep, sink)
     flops = ctypes.c_longlong(0)
     _check("fp8bs_mfma_ceiling", lib.fp8bs_mfma_ceiling(_ptr(A), _ptr(B_prep), M, N, K, iters, _ptr(sink),
                                                         sink.numel(), ctypes.byref(flops), _stream(stream)))

@@ -303,6 +303,8 @@ size_t fp8bs_prep_weight_bytes(int N, int K)
     return (size_t)N * (size_t)K;
 }
 
+size_t fp8bs_prep_bytes(int N, int K) { return fp8bs_prep_weight_bytes(N, K); }
+
 int fp8bs_prep_weights(const void* B, void* B_prep, int N, int K, hipStream_t stream)
 {
     if (N < 64 || N % 64 != 0 || K < 128 || K % 128 != 0)
@@ -354,6 +356,8 @@ size_t fp8mx_packed_scale_bytes(int rows, int K)
         return 0;
     return (size_t)rows * (size_t)(K / 32);
 }
+
+size_t fp8mx_scale_bytes(int rows, int K) { return fp8mx_packed_scale_bytes(rows, K); }
 
 int fp8mx_pack_a_scale(const void* a_e8m0, void* a_scale_packed, int M, int K, hipStream_t stream)
 {

@@ -392,7 +392,7 @@ decode_lds_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scal
 }
 
 template <int ROUTE, int SI>
-void launch_one(int variant, const GemmArgs& a)
+hipError_t launch_one(int variant, const GemmArgs& a)
 {
     const int chunks = (a.M + kDecodeMaxRows - 1) / kDecodeMaxRows;
     const uint8_t* A = (const uint8_t*)a.A;
@@ -400,15 +400,16 @@ void launch_one(int variant, const GemmArgs& a)
     uint16_t* C = (uint16_t*)a.C;
     if (variant == kDecodeLdsPair) {
         if constexpr (SI <= 2)
-            hipLaunchKernelGGL((decode_lds_kernel<ROUTE, SI, 2>), dim3(a.N / 32, chunks),
-                               dim3(waves_for<SI, 2>() * 64), 0, a.stream, A, a.a_scale, B, a.b_scale, C, a.M, a.N,
-                               a.K);
-    } else if (variant == kDecodeLds)
-        hipLaunchKernelGGL((decode_lds_kernel<ROUTE, SI, 1>), dim3(a.N / 16, chunks), dim3(waves_for<SI, 1>() * 64),
-                           0, a.stream, A, a.a_scale, B, a.b_scale, C, a.M, a.N, a.K);
-    else
-        hipLaunchKernelGGL((decode_direct_kernel<ROUTE, SI>), dim3(a.N / 16, chunks), dim3(kDecodeWaves * 64), 0, a.stream,
-                           A, a.a_scale, B, a.b_scale, C, a.M, a.N, a.K);
+            return launch_kernel(decode_lds_kernel<ROUTE, SI, 2>, dim3(a.N / 32, chunks), dim3(waves_for<SI, 2>() * 64),
+                                 a.stream, A, a.a_scale, B, a.b_scale, C, a.M, a.N, a.K);
+        else
+            return hipErrorInvalidValue;
+    }
+    if (variant == kDecodeLds)
+        return launch_kernel(decode_lds_kernel<ROUTE, SI, 1>, dim3(a.N / 16, chunks), dim3(waves_for<SI, 1>() * 64),
+                             a.stream, A, a.a_scale, B, a.b_scale, C, a.M, a.N, a.K);
+    return launch_kernel(decode_direct_kernel<ROUTE, SI>, dim3(a.N / 16, chunks), dim3(kDecodeWaves * 64), a.stream,
+                         A, a.a_scale, B, a.b_scale, C, a.M, a.N, a.K);
 }
 
 template <int ROUTE>
@@ -416,19 +417,14 @@ hipError_t launch_route(int si, int variant, const GemmArgs& a)
 {
     switch (si) {
     case 1:
-        launch_one<ROUTE, 1>(variant, a);
-        break;
+        return launch_one<ROUTE, 1>(variant, a);
     case 2:
-        launch_one<ROUTE, 2>(variant, a);
-        break;
+        return launch_one<ROUTE, 2>(variant, a);
     case 3:
-        launch_one<ROUTE, 3>(variant, a);
-        break;
+        return launch_one<ROUTE, 3>(variant, a);
     default:
-        launch_one<ROUTE, 4>(variant, a);
-        break;
+        return launch_one<ROUTE, 4>(variant, a);
     }
-    return hipGetLastError();
 }
 
 }  // namespace

@@ -45,6 +45,7 @@
 #include "device.hpp"
 #include "launch.hpp"
 
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -841,18 +842,23 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
 
 // ---- host side ---------------------------------------------------------------------------
 
+// Compute units of each device, read once per device (std::call_once: the first calls may come
+// from several host threads at once).
+constexpr int kMaxDevices = 64;
+
 int device_cus()
 {
-    static int cus[64] = {0};
+    static std::once_flag once[kMaxDevices];
+    static int cus[kMaxDevices];
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
         return 256;
-    if (cus[dev] == 0) {
+    std::call_once(once[dev], [dev] {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
             n = 256;
         cus[dev] = n;
-    }
+    });
     return cus[dev];
 }
 
@@ -860,24 +866,28 @@ template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES, int PP>
 static hipError_t launch_tile(const GemmArgs& a, const GemmConfig& c)
 {
     using T = Tile<ROUTE, BM, BN, WM, WN, STAGES, PP>;
-    // workgroups that fit on one CU at once (LDS and registers), once per instantiation
-    static const int per_cu = [] {
+    auto kernel = gemm_kernel<ROUTE, BM, BN, WM, WN, STAGES, PP>;
+    // workgroups of this kernel that fit on one CU at once (LDS and registers), once per device
+    static std::once_flag once[kMaxDevices];
+    static int per_cu[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::call_once(once[dev], [&] {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_kernel<ROUTE, BM, BN, WM, WN, STAGES, PP>,
-                                                         T::kThreads, 0) != hipSuccess || n < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, T::kThreads, 0) != hipSuccess || n < 1)
             n = 1;
-        return n;
-    }();
+        per_cu[dev] = n;
+    });
     const int tiles_m = (a.M + BM - 1) / BM;
     const int tiles_n = a.N / BN;
     const int T_total = tiles_m * tiles_n;
-    int grid = device_cus() * per_cu;
+    int grid = device_cus() * per_cu[dev];
     if (c.persistent == 0 || grid > T_total)
         grid = T_total;
-    hipLaunchKernelGGL((gemm_kernel<ROUTE, BM, BN, WM, WN, STAGES, PP>), dim3(grid), dim3(T::kThreads), 0, a.stream,
-                       (const uint8_t*)a.A, a.a_scale, (const uint8_t*)a.B, a.b_scale, (uint16_t*)a.C, a.M, a.N,
-                       a.K, tiles_m, tiles_n, c.group_m > 0 ? c.group_m : 1, c.xcd_remap);
-    return hipGetLastError();
+    return launch_kernel(kernel, dim3(grid), dim3(T::kThreads), a.stream, (const uint8_t*)a.A, a.a_scale,
+                         (const uint8_t*)a.B, a.b_scale, (uint16_t*)a.C, a.M, a.N, a.K, tiles_m, tiles_n,
+                         c.group_m > 0 ? c.group_m : 1, c.xcd_remap);
 }
 
 // Instantiated shapes: {BM, BN, WM, WN, STAGES, ping-pong}. Index = GemmConfig::variant.

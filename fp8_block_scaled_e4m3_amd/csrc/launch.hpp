@@ -4,7 +4,25 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+
 namespace fp8bs {
+
+// Enqueue kernel<<<grid, block, 0, stream>>>(args...) and return the status of this launch
+// alone (hipLaunchKernel's own return value): an error that earlier, unrelated work left
+// pending in the runtime is neither reported as this launch's failure nor cleared.
+template <typename... P, typename... A>
+inline hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream, A... args)
+{
+    static_assert(sizeof...(P) == sizeof...(A), "one argument per kernel parameter");
+    std::tuple<P...> values{static_cast<P>(args)...};
+    void* ptrs[sizeof...(P) > 0 ? sizeof...(P) : 1];
+    std::apply([&](auto&... v) {
+        int i = 0;
+        ((ptrs[i++] = (void*)&v), ...);
+    }, values);
+    return hipLaunchKernel((const void*)kernel, grid, block, ptrs, 0, stream);
+}
 
 enum { kRouteBS = 0, kRouteMX = 1, kRoutePT = 2 };
 // Small-M kernel only: route MX with the packed activation scales of fp8mx_pack_a_scale (M % 64

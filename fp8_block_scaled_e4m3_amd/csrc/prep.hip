@@ -40,9 +40,8 @@ hipError_t launch_pack_scales(const void* e8m0, void* packed, int rows, int K, i
         return hipSuccess;
     const int threads = 256;
     const unsigned blocks = (unsigned)((total + threads - 1) / threads);
-    hipLaunchKernelGGL(pack_scales_kernel, dim3(blocks), dim3(threads), 0, stream,
-                       (const uint8_t*)e8m0, (uint32_t*)packed, rows, K, permute);
-    return hipGetLastError();
+    return launch_kernel(pack_scales_kernel, dim3(blocks), dim3(threads), stream, (const uint8_t*)e8m0,
+                         (uint32_t*)packed, rows, K, permute);
 }
 
 // Prepared weights: B [N, K] with the rows of every 64-row window reordered by
@@ -70,9 +69,8 @@ hipError_t launch_prep_weights(const void* B, void* B_prep, int N, int K, hipStr
         return hipSuccess;
     const int threads = 256;
     const unsigned blocks = (unsigned)((total + threads - 1) / threads);
-    hipLaunchKernelGGL(prep_weights_kernel, dim3(blocks), dim3(threads), 0, stream, (const uint8_t*)B,
-                       (uint8_t*)B_prep, N, K);
-    return hipGetLastError();
+    return launch_kernel(prep_weights_kernel, dim3(blocks), dim3(threads), stream, (const uint8_t*)B,
+                         (uint8_t*)B_prep, N, K);
 }
 
 }  // namespace fp8bs

@@ -69,9 +69,8 @@ hipError_t launch_mfma_ceiling(const void* A, const void* B_prep, int M, int N, 
         return hipErrorInvalidValue;
     if (flops)
         *flops = (long long)wgs * waves_per_wg * iters * 16 * (2LL * 16 * 16 * 128);
-    hipLaunchKernelGGL(mfma_ceiling_kernel, dim3(wgs), dim3(kProbeThreads), 0, stream, (const uint8_t*)A,
-                       (const uint8_t*)B_prep, M, N, K, iters, sink);
-    return hipGetLastError();
+    return launch_kernel(mfma_ceiling_kernel, dim3(wgs), dim3(kProbeThreads), stream, (const uint8_t*)A,
+                         (const uint8_t*)B_prep, M, N, K, iters, sink);
 }
 
 }  // namespace fp8bs

@@ -191,22 +191,18 @@ hipError_t launch_quantize(int route, const void* x, int in_bf16, void* codes, v
         const int MB = (M + 63) / 64;
         const int grid = MB * (K >> 7);  // M * K < 2^31, so this fits
         if (in_bf16)
-            hipLaunchKernelGGL(quantize_bs_kernel<1>, dim3(grid), dim3(kQuantThreads), 0, stream, x,
-                               (uint8_t*)codes, (float*)scales, M, K, MB);
-        else
-            hipLaunchKernelGGL(quantize_bs_kernel<0>, dim3(grid), dim3(kQuantThreads), 0, stream, x,
-                               (uint8_t*)codes, (float*)scales, M, K, MB);
-    } else {
-        const long long groups = (long long)M * (K >> 5);
-        const int grid = (int)((groups + 511) / 512);
-        if (in_bf16)
-            hipLaunchKernelGGL(quantize_mx_kernel<1>, dim3(grid), dim3(kQuantThreads), 0, stream, x,
-                               (uint8_t*)codes, (uint8_t*)scales, groups);
-        else
-            hipLaunchKernelGGL(quantize_mx_kernel<0>, dim3(grid), dim3(kQuantThreads), 0, stream, x,
-                               (uint8_t*)codes, (uint8_t*)scales, groups);
+            return launch_kernel(quantize_bs_kernel<1>, dim3(grid), dim3(kQuantThreads), stream, x, (uint8_t*)codes,
+                                 (float*)scales, M, K, MB);
+        return launch_kernel(quantize_bs_kernel<0>, dim3(grid), dim3(kQuantThreads), stream, x, (uint8_t*)codes,
+                             (float*)scales, M, K, MB);
     }
-    return hipGetLastError();
+    const long long groups = (long long)M * (K >> 5);
+    const int grid = (int)((groups + 511) / 512);
+    if (in_bf16)
+        return launch_kernel(quantize_mx_kernel<1>, dim3(grid), dim3(kQuantThreads), stream, x, (uint8_t*)codes,
+                             (uint8_t*)scales, groups);
+    return launch_kernel(quantize_mx_kernel<0>, dim3(grid), dim3(kQuantThreads), stream, x, (uint8_t*)codes,
+                         (uint8_t*)scales, groups);
 }
 
 }  // namespace fp8bs

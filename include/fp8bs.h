@@ -32,7 +32,9 @@
  *     the host, so calls may be captured into a HIP graph.
  *   - Every call returns an fp8bs_status. Pointer, shape and alignment checks run on the host
  *     before anything is launched; on failure nothing is enqueued and outputs are untouched.
- *     Launch failures are reported as FP8BS_E_HIP. No call aborts or throws.
+ *     A failure of the call's own kernel launch is reported as FP8BS_E_HIP (an error that
+ *     earlier work left pending in the HIP runtime is neither reported nor cleared). No call
+ *     aborts or throws.
  *   - Shapes that break a constraint are rejected, never padded (page "aiter PR #6370",
  *     Constraints).
  */
@@ -68,8 +70,10 @@ const char *fp8bs_strerror(int status);
  * 2 and 6: weights are laid out once at set-up and the buffers reused every call).
  * ------------------------------------------------------------------------------------------ */
 
-/* Bytes of the prepared weight buffer for an N x K e4m3 weight (same for both routes). */
+/* Bytes of the prepared weight buffer for an N x K e4m3 weight (same for both routes); 0 when
+ * N or K is not positive. fp8bs_prep_bytes is the same function under a shorter name. */
 size_t fp8bs_prep_weight_bytes(int N, int K);
+size_t fp8bs_prep_bytes(int N, int K);
 
 /* Lay out B [N,K] (e4m3, row-major) into B_prep, the opaque layout that fp8bs_gemm and
  * fp8mx_gemm consume. B_prep must hold fp8bs_prep_weight_bytes(N, K) bytes and must not
@@ -125,8 +129,10 @@ int fp8bs_gemm(const void *A, const float *a_scale, const void *B_prep, const fl
  * Route MX.
  * ------------------------------------------------------------------------------------------ */
 
-/* Bytes of a packed ue8m0 scale buffer for `rows` rows and K columns (K/32 scales per row). */
+/* Bytes of a packed ue8m0 scale buffer for `rows` rows and K columns (K/32 scales per row); 0
+ * when rows or K is not positive. fp8mx_scale_bytes is the same function under a shorter name. */
 size_t fp8mx_packed_scale_bytes(int rows, int K);
+size_t fp8mx_scale_bytes(int rows, int K);
 
 /* Pack B's ue8m0 scales b_e8m0 [N, K/32] (uint8, biased by 127, row-major) into the
  * K-block-major, four-to-a-dword layout the scaled instruction consumes (page "aiter PR

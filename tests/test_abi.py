@@ -165,3 +165,124 @@ def test_select_config_rejects_bad_input(fb):
     assert fb.lib.fp8bs_select_config(1, 100, 128, 256, ctypes.byref(cfg)) == 2
     assert fb.lib.fp8bs_select_config(7, 128, 128, 256, ctypes.byref(cfg)) == 4
     assert fb.lib.fp8bs_select_config(0, 128, 128, 256, None) == 1
+
+
+def test_small_m_limits_rejected_on_the_host(fb):
+    """More than 65535 chunks of 64 rows, and K below the MX minimum, are rejected before
+    anything is launched: placeholder pointers are never dereferenced."""
+    p = 0x10000
+    too_many = 64 * 65535 + 1
+    cfg = fb.Config()
+    cfg.small_m = 1
+    assert fb.lib.fp8bs_gemm_with_config(p, p, p, p, p, too_many, 256, 256, ctypes.byref(cfg), None) == 4
+    assert fb.lib.fp8pt_gemm_with_config(p, p, p, p, p, too_many, 256, 256, ctypes.byref(cfg), None) == 4
+    assert fb.lib.fp8mx_gemm_small_m(p, p, p, p, p, too_many, 256, 256, None) == 2
+    assert fb.lib.fp8mx_gemm_small_m(p, p, p, p, p, 16, 256, 128, None) == 2
+    pair = fb.Config()
+    pair.small_m = 4  # two weight sub-tiles per workgroup: at most 32 rows per chunk
+    assert fb.lib.fp8bs_gemm_with_config(p, p, p, p, p, 33, 256, 256, ctypes.byref(pair), None) == 4
+    bad = fb.Config()
+    bad.small_m = 5
+    assert fb.lib.fp8bs_gemm_with_config(p, p, p, p, p, 8, 256, 256, ctypes.byref(bad), None) == 4
+
+
+def test_offsets_past_32_bits_rejected(fb):
+    p = 0x10000
+    assert fb.lib.fp8bs_gemm(p, p, p, p, p, 1 << 21, 128, 1024, None) == 2  # M*K = 2^31
+    assert fb.lib.fp8bs_gemm(p, p, p, p, p, 16, 1 << 21, 1024, None) == 2   # N*K = 2^31
+
+
+# ---- the Python binding checks every tensor before the library sees it ------------------------
+
+def _cpu_bs(M, N, K):
+    import torch
+    return (torch.zeros((M, K), dtype=torch.uint8), torch.ones((K // 128, M)), torch.zeros(N * K, dtype=torch.uint8),
+            torch.ones((N // 128, K // 128)), torch.zeros((M, N), dtype=torch.bfloat16))
+
+
+def test_binding_rejects_missized_operands(fb):
+    import torch
+    M, N, K = 64, 256, 512
+    A, sa, Bp, sb, C = _cpu_bs(M, N, K)
+    bad = {
+        "a_scale in [M, K/128] (the natural layout)": dict(a_scale=torch.ones((M, K // 128))),
+        "C with fewer rows": dict(C=torch.zeros((M - 1, N), dtype=torch.bfloat16)),
+        "C in fp32": dict(C=torch.zeros((M, N), dtype=torch.float32)),
+        "B_prep for fewer weight rows": dict(B_prep=torch.zeros((N - 128) * K, dtype=torch.uint8)),
+        "b_scale transposed": dict(b_scale=torch.ones((K // 128, N // 128))),
+        "A in bf16": dict(A=torch.zeros((M, K), dtype=torch.bfloat16)),
+        "a_scale in fp64": dict(a_scale=torch.ones((K // 128, M), dtype=torch.float64)),
+    }
+    for what, repl in bad.items():
+        args = dict(A=A, a_scale=sa, B_prep=Bp, b_scale=sb, C=C)
+        args.update(repl)
+        with pytest.raises(ValueError):
+            fb.fp8bs_gemm(**args)
+        with pytest.raises(ValueError):
+            fb.fp8bs_gemm_with_config(config=fb.Config(), **args)
+    # every size right, but host memory: refused before any call
+    with pytest.raises(ValueError, match="device tensors"):
+        fb.fp8bs_gemm(A, sa, Bp, sb, C)
+
+
+def test_binding_rejects_missized_mx_pt_and_quantiser_operands(fb):
+    import torch
+    M, N, K = 64, 256, 512
+    A = torch.zeros((M, K), dtype=torch.uint8)
+    C = torch.zeros((M, N), dtype=torch.bfloat16)
+    Bp = torch.zeros(N * K, dtype=torch.uint8)
+    pa = torch.zeros(M * K // 32, dtype=torch.uint8)
+    pb = torch.zeros(N * K // 32, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="b_scale_packed"):
+        fb.fp8mx_gemm(A, pa, Bp, pb[:-4], C)
+    with pytest.raises(ValueError, match="a_scale_packed"):
+        fb.fp8mx_gemm(A, pa[: M * K // 64], Bp, pb, C)
+    with pytest.raises(ValueError, match="a_e8m0"):
+        fb.fp8mx_gemm_small_m(A, pa, Bp, pb, C)  # the small-M entry takes [M, K/32] bytes
+    with pytest.raises(ValueError, match="device tensors"):
+        fb.fp8mx_gemm_small_m(A, pa.view(M, K // 32), Bp, pb, C)
+    with pytest.raises(ValueError, match="a_scale"):
+        fb.fp8pt_gemm(A, torch.ones(M + 1), Bp, torch.ones(N), C)
+    with pytest.raises(ValueError, match="b_scale"):
+        fb.fp8pt_gemm(A, torch.ones(M), Bp, torch.ones((N // 128, K // 128)), C)
+    x = torch.zeros((M, K), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="a_scale"):
+        fb.fp8bs_quantize_act(x, A, torch.ones((M, K // 128)))
+    with pytest.raises(ValueError, match="A_codes"):
+        fb.fp8mx_quantize_act(x, A[:, : K // 2], torch.zeros((M, K // 32), dtype=torch.uint8))
+    with pytest.raises(ValueError, match="dtype"):
+        fb.fp8bs_quantize_act(x.to(torch.float16), A, torch.ones((K // 128, M)))
+    with pytest.raises(ValueError, match="B_prep"):
+        fb.fp8bs_prep_weights(torch.zeros((N, K), dtype=torch.uint8), torch.zeros(N * K // 2, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="b_e8m0"):
+        fb.fp8mx_prep_weights(torch.zeros((N, K), dtype=torch.uint8), torch.zeros((N, K // 16), dtype=torch.uint8),
+                              Bp, pb)
+
+
+# ---- names the hot-path contract lists, or the recorded name that serves each ------------------
+
+# The survey's boundary names the calls below. Where this library's name differs, the value is
+# the exported call that provides it (the difference is recorded in the design notes).
+CONTRACT_CALLS = {
+    "fp8bs_gemm": "fp8bs_gemm",
+    "fp8mx_gemm": "fp8mx_gemm",
+    "fp8bs_prep_bytes": "fp8bs_prep_bytes",
+    "fp8bs_prep_weights": "fp8bs_prep_weights",
+    "fp8mx_prep_weights": "fp8mx_prep_weights",
+    "fp8mx_pack_a_scale": "fp8mx_pack_a_scale",
+    "fp8mx_scale_bytes": "fp8mx_scale_bytes",
+    "fp8bs_select_config": "fp8bs_select_config",
+    "fp8bs_gemm_with_config": "fp8bs_gemm_with_config",
+    "fp8mx_gemm_with_config": "fp8mx_gemm_with_config",
+    "fp8bs_strerror": "fp8bs_strerror",
+    "fp8bs_version": "fp8bs_version",
+}
+
+
+def test_contract_calls_are_exported(fb):
+    handle = ctypes.CDLL(fb.LIBRARY)
+    declared = _declared()
+    for want, name in CONTRACT_CALLS.items():
+        assert hasattr(handle, name) and name in declared, f"{want}: {name} not exported"
+    assert fb.fp8bs_prep_bytes(256, 512) == fb.fp8bs_prep_weight_bytes(256, 512) == 256 * 512
+    assert fb.fp8mx_scale_bytes(128, 512) == fb.fp8mx_packed_scale_bytes(128, 512) == 128 * 16

@@ -64,9 +64,15 @@ def test_zero_rows_is_noop(fb):
 
 
 def test_python_wrapper_raises(fb):
-    A, sa, B, sb, C = _bufs(128, 128, 256)
-    with pytest.raises(fb.Fp8bsError):
-        fb.fp8bs_gemm(A, sa, B, sb, torch.empty((128, 100), dtype=torch.bfloat16, device=A.device))
+    """A shape the library rejects (N % 128 != 0) surfaces as Fp8bsError with its status code."""
+    A, sa, _, sb, _ = _bufs(128, 128, 256)
+    B = torch.zeros((100, 256), dtype=torch.uint8, device=A.device)
+    C = torch.full((128, 100), 7.0, dtype=torch.bfloat16, device=A.device)
+    with pytest.raises(fb.Fp8bsError) as e:
+        fb.fp8bs_gemm(A, sa, B, sb, C)
+    assert e.value.status == 2
+    torch.cuda.synchronize()
+    assert torch.all(C == 7.0)
 
 
 def test_zero_rows_is_noop_every_route(fb):

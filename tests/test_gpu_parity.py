@@ -44,6 +44,15 @@ def test_mx_small_full(fb, oracle, M, N, K, seed):
     parity(got, ref, f"mx {M}x{N}x{K} seed {seed}")
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_tiny_workload_full_every_seed(fb, oracle, seed):
+    """The tiny workload (128 x 256 x 512) in full for seeds 0-3, through the plain entry point
+    and its own kernel choice (page "Flydsl Fp8 Blockscale Gemm", front matter: seeds 0-3)."""
+    cfg, x = _inputs("tiny", seed)
+    got = _run(fb, cfg, x)
+    parity(got, _ref(oracle, cfg, x), f"tiny full C seed {seed}")
+
+
 def _sampled(M, N, seed, n=512):
     return workload.sample_indices(M, n, seed), workload.sample_indices(N, n, seed + 1)
 

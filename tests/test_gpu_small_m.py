@@ -205,21 +205,5 @@ def test_small_m_rejects(fb):
     with pytest.raises(fb.Fp8bsError) as e:
         _run_bs_cfg(fb, z, _small(fb, PAIR))
     assert e.value.status == 4
-    d = dev()
-    A = torch.zeros((65, 256), dtype=torch.uint8, device=d)
-    buf = torch.zeros(1 << 16, dtype=torch.uint8, device=d)
-    fbuf = torch.ones(1 << 14, dtype=torch.float32, device=d)
-    C = torch.full((65, 256), 3.0, dtype=torch.bfloat16, device=d)
-    # more than 65535 chunks of 64 rows: rejected before anything is launched (the small
-    # buffers are never touched)
-    too_many = 64 * 65535 + 1
-    cfg = _small(fb, AUTO)
-    import ctypes
-    assert fb.lib.fp8bs_gemm_with_config(A.data_ptr(), fbuf.data_ptr(), buf.data_ptr(), fbuf.data_ptr(),
-                                         C.data_ptr(), too_many, 256, 256, ctypes.byref(cfg), None) == 4
-    assert fb.lib.fp8mx_gemm_small_m(A.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), C.data_ptr(),
-                                     too_many, 256, 256, None) == 2
-    assert fb.lib.fp8mx_gemm_small_m(A.data_ptr(), buf.data_ptr(), buf.data_ptr(), buf.data_ptr(), C.data_ptr(),
-                                     16, 256, 128, None) == 2
-    torch.cuda.synchronize()
-    assert torch.all(C == 3.0)
+    # shapes past the small-M kernel's chunk limit are rejected on the host: covered on the CPU
+    # with placeholder pointers (tests/test_abi.py), so no device call here gets a short buffer

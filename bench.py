@@ -401,6 +401,17 @@ def profile_mode(name: str, steps: int, warmup: int) -> int:
         elif kind == "small_m":
             _, wl, rows = name.split(":")
             case = Case(wl, 0, stream, rows=int(rows))
+        elif "@" in name:
+            # NAME@field=value,...: the library's configuration for NAME with those fields replaced
+            import fp8_block_scaled_e4m3_amd as fb
+            wl, over = name.split("@", 1)
+            base = Case(wl, 0, stream)
+            cfg = fb.Config(**{k: v for k, v in base.config.items()})
+            for kv in over.split(","):
+                k, v = kv.split("=")
+                setattr(cfg, k, int(v))
+            base.free()
+            case = Case(wl, 0, stream, config=cfg)
         elif name.startswith("twin:"):
             case = Case(name[len("twin:"):], 0, stream, twin=True)
         elif name.startswith("ksweep:"):
@@ -519,7 +530,7 @@ def ksweep_mode(M: int, N: int, Ks, stream) -> int:
 SWEEP_TILES = [(256, 256, 2, 4, 2, 0), (256, 128, 4, 2, 3, 2), (128, 256, 2, 4, 3, 2), (128, 128, 2, 2, 3, 2)]
 
 
-def tile_sweep_mode(name: str, stream, group_ms=(1, 2, 4, 8, 16), tiles=None) -> int:
+def tile_sweep_mode(name: str, stream, group_ms=(2, 4, 8, 16), tiles=None) -> int:
     """Every tile order (group_m x XCD mapping) for each tile in `tiles` on one workload, through
     the *_with_config entry. The library's own choice is checked against the oracle first; every
     other configuration must give the same bits (all do the same per-element arithmetic)."""
@@ -587,19 +598,164 @@ def summarize_pmc(dirs: list[str], match: str = "gemm_kernel") -> int:
     for (d, name), v in vals.items():
         v = sorted(v)
         med.setdefault(name, v[len(v) // 2])
-    cus, simds = 256, 1024
+    cus, simds, xcds = 256, 1024, 8
     out = {"kernel": kernel, "counters_median_per_dispatch": med}
     g = med.get("GRBM_GUI_ACTIVE")
     if g:
+        g = g / xcds  # one XCD's busy cycles: the counter is summed over the XCDs
+        out["gpu_cycles"] = round(g)
         if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
             out["mfma_busy"] = round(med["SQ_VALU_MFMA_BUSY_CYCLES"] / (g * simds), 4)
         if "SQ_ACTIVE_INST_VALU" in med:
             out["valu_busy"] = round(med["SQ_ACTIVE_INST_VALU"] / (g * cus), 4)
+    if med.get("SQ_WAVE_CYCLES"):
+        if "SQ_WAIT_ANY" in med:
+            out["wait_any_share"] = round(med["SQ_WAIT_ANY"] / med["SQ_WAVE_CYCLES"], 4)
+        if "SQ_WAIT_INST_LDS" in med:
+            out["wait_inst_lds_share"] = round(med["SQ_WAIT_INST_LDS"] / med["SQ_WAVE_CYCLES"], 4)
     if med.get("SQ_LDS_IDX_ACTIVE"):
         out["lds_bank_conflict_share"] = round(med.get("SQ_LDS_BANK_CONFLICT", 0.0) / med["SQ_LDS_IDX_ACTIVE"], 5)
     if med.get("SQ_INSTS_MFMA"):
         out["valu_insts_per_mfma"] = round(med.get("SQ_INSTS_VALU", 0.0) / med["SQ_INSTS_MFMA"], 3)
     print(json.dumps(out), flush=True)
+    return 0
+
+
+def _trace_rows(d: str) -> list[dict]:
+    rows = []
+    for path in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    return rows
+
+
+def profile_md(name: str, trace_dir: str, pmc_dirs: list[str], timed: int) -> int:
+    """Markdown summary of one workload's rocprofv3 runs (made by the commands it lists): kernel
+    statistics from the kernel trace, the average over the last `timed` launches of the profiled
+    kernel, the byte counters (from profiles/traffic.json) and the SQ counter passes."""
+    kind = profile_kind(name)
+    match = PROFILE_KERNELS[kind][0]
+    rows = _trace_rows(trace_dir)
+    stats: dict[str, list[int]] = {}
+    for r in rows:
+        stats.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    mine = [r for r in rows if match in r["Kernel_Name"]]
+    if not mine:
+        print(f"no {match} launches in {trace_dir}", file=sys.stderr)
+        return 2
+    kname = mine[-1]["Kernel_Name"]
+    short = kname.split("(")[0]
+    last = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in mine[-timed:]]
+    r0 = mine[-1]
+    meta = {}
+    for cand in glob.glob(os.path.join(trace_dir, "**", "profile.json"), recursive=True):
+        meta = json.load(open(cand))
+    lines = [f"# {match.rstrip('_')} on the {name} workload -- rocprofv3 summary", "",
+             f"Kernel: `{short}` (config {meta.get('config')}); grid {r0.get('Grid_Size_X', '?')} x "
+             f"{r0.get('Grid_Size_Y', '?')} work-items in workgroups of {r0.get('Workgroup_Size_X', '?')}, "
+             f"VGPR_Count {r0.get('VGPR_Count', '?')} + {r0.get('Accum_VGPR_Count', '?')} AGPRs, "
+             f"{r0.get('SGPR_Count', '?')} SGPRs, {r0.get('LDS_Block_Size', '?')} B LDS, scratch "
+             f"{r0.get('Scratch_Size', '?')} B.", "",
+             "Commands (run from /tmp with TMPDIR=/tmp; R = repository root; each --profile run prints its",
+             "parameters as JSON on stdout, kept as profile.json beside the output):", "", "```",
+             f"rocprofv3 --kernel-trace --stats -d OUT/trace -o run --output-format csv -- python3 R/bench.py "
+             f"--profile {name} --steps {timed} --warmup 400",
+             f"rocprofv3 --pmc FETCH_SIZE -d OUT/fetch -o run --output-format csv -- python3 R/bench.py --profile {name} "
+             "--steps 10 --warmup 5",
+             f"rocprofv3 --pmc WRITE_SIZE -d OUT/write -o run --output-format csv -- python3 R/bench.py --profile {name} "
+             "--steps 10 --warmup 5",
+             "python3 R/bench.py --ingest-counters OUT/fetch OUT/write   # -> profiles/traffic.json"]
+    for p in sorted(PMC_PASSES):
+        if any(d.endswith(f"_{p}") for d in pmc_dirs):
+            lines.append(f"rocprofv3 --pmc $(python3 R/bench.py --pmc-pass {p}) -d OUT/pmc_{p} -o run --output-format csv "
+                         f"-- python3 R/bench.py --profile {name} --steps 10 --warmup 5")
+    lines += [f"python3 R/bench.py --profile-md {name} OUT/trace {' '.join('OUT/' + os.path.basename(d) for d in pmc_dirs)}",
+              "```", "", "## Kernel statistics (all launches, including the warmup ones)", "",
+              "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
+    for k, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{k.split('(')[0][:80]}` | {len(v)} | {sum(v) // len(v)} | {min(v)} | {max(v)} |")
+    srt = sorted(last)
+    lines += ["", f"Average over the last {len(last)} (timed) launches from the kernel trace: "
+                  f"**{sum(last) / len(last) / 1e3:.2f} us** (median {srt[len(srt) // 2] / 1e3:.2f} us). The same process "
+                  f"measured {meta.get('avg_launch_us', '?')} us per launch with HIP events on its stream over the timed "
+                  "launches. Early launches run while the GPU clock ramps up, so the all-launch average is higher."]
+    rec = json.load(open(TRAFFIC_RECORD)).get(name) if os.path.exists(TRAFFIC_RECORD) else None
+    if rec:
+        lines += ["", "## HBM traffic per launch (--pmc, separate runs)", "",
+                  "| counter | raw per launch (bytes) | calibration copy raw (bytes, true 268435456) | scale | scaled bytes per launch |",
+                  "|---|---|---|---|---|"]
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            e = rec["counters"][c]
+            lines.append(f"| {c} | {e['raw_bytes_per_launch']:.0f} | {e['copy_raw_bytes']:.0f} | {e['scale']:.4f} | "
+                         f"{e['bytes_per_launch']:.0f} |")
+        lines += ["", f"traffic = {rec['traffic_bytes']} bytes per launch (kernel source sha256 "
+                      f"{rec['kernel_source_sha256'][:16]})."]
+    if pmc_dirs:
+        import io
+        import contextlib
+        buf = io.StringIO()
+        with contextlib.redirect_stdout(buf):
+            summarize_pmc(pmc_dirs, match)
+        summ = json.loads(buf.getvalue())
+        lines += ["", "## SQ counters (median per dispatch over the profiled launches; sums over all XCDs)", "",
+                  "| counter | value |", "|---|---|"]
+        for c, v in sorted(summ["counters_median_per_dispatch"].items()):
+            lines.append(f"| {c} | {v:.0f} |")
+        lines += ["", "Derived (GRBM_GUI_ACTIVE is summed over the 8 XCDs: one XCD's active cycles are an eighth "
+                      "of it; SQ_WAVE_CYCLES and the wait counters are in units of 4 cycles):", ""]
+        for k in ("gpu_cycles", "mfma_busy", "valu_busy", "lds_bank_conflict_share", "valu_insts_per_mfma",
+                  "wait_any_share", "wait_inst_lds_share"):
+            if k in summ:
+                lines.append(f"- {k}: {summ[k]}")
+    print("\n".join(lines))
+    return 0
+
+
+def sweep_md(path: str) -> int:
+    """Markdown of a --ksweep or --tile-sweep JSON line (the file holds bench.py's stdout)."""
+    with open(path) as f:
+        d = json.loads(f.read().strip().splitlines()[-1])
+    out = []
+    if d["mode"] == "ksweep":
+        ks = ",".join(str(pt["K"]) for pt in d["routes"]["bs"]["points"])
+        out += [f"# K sweep at M = {d['M']}, N = {d['N']} (routes BS and PT)", "",
+                "Command (R = repository root):", "", "```",
+                f"python3 R/bench.py --ksweep --ksweep-shape {d['M']},{d['N']} --ksweep-k {ks} > OUT/ksweep.json",
+                "python3 R/bench.py --sweep-md OUT/ksweep.json", "```", "",
+                "Each point: the library's own configuration for the shape, parity against the oracle on 8 sampled",
+                "rows and 8 sampled columns checked before timing, then the minimum over 3 runs of the median",
+                "per-launch time (5 groups of back-to-back launches per run, HIP events on the stream).",
+                "Least-squares fit: time = fixed + slope x (K / 128).", "",
+                "| route | K | K blocks | us | median us | TFLOP/s | parity |", "|---|---|---|---|---|---|---|"]
+        for r, v in d["routes"].items():
+            for pt in v["points"]:
+                out.append(f"| {r} | {pt['K']} | {pt['k_blocks']} | {pt['us']} | {pt['us_med']} | {pt['tflops']} | "
+                           f"{pt['parity_passed']} |")
+        out += ["", "| route | fixed us | us per K block | max residual us |", "|---|---|---|---|"]
+        for r, v in d["routes"].items():
+            out.append(f"| {r} | {v['fixed_us']} | {v['us_per_k_block']} | {v['max_residual_us']} |")
+        cfg = d["routes"]["bs"]["points"][0]["config"]
+        out += ["", f"Configuration (both routes): {cfg}."]
+    else:
+        rows = d["rows"]
+        sel = rows[0]
+        out += [f"# Tile and tile-order sweep on {d['workload']}", "",
+                "Command (R = repository root):", "", "```",
+                f"python3 R/bench.py --tile-sweep {d['workload']} > OUT/tiles.json",
+                "python3 R/bench.py --sweep-md OUT/tiles.json", "```", "",
+                "Every configuration through the *_with_config entry on the same inputs; the library's own",
+                f"choice was checked against the oracle first (sampled parity passed: {d['parity']['passed']}) and",
+                "every other configuration gave the same bits (bitwise_equal). Times: minimum over 3 runs of the",
+                "median per-launch time.", "",
+                f"Selected: {sel['block_m']}x{sel['block_n']} waves {sel['waves_m']}x{sel['waves_n']}, {sel['stages']} "
+                f"stages, schedule {sel['pingpong']}, group_m {sel['group_m']}, XCD mapping {sel['xcd_remap']}: "
+                f"**{sel['us']} us**.", "",
+                "| tile | waves | stages | schedule | group_m | XCD mapping | us | same bits |", "|---|---|---|---|---|---|---|---|"]
+        for r in sorted(rows[1:], key=lambda r: r["us"]):
+            out.append(f"| {r['tile']} | {r['waves']} | {r['stages']} | {r['pingpong']} | {r['group_m']} | "
+                       f"{r['xcd_remap']} | {r['us']} | {r['bitwise_equal']} |")
+    print("\n".join(out))
     return 0
 
 
@@ -621,11 +777,19 @@ def main() -> int:
     ap.add_argument("--summarize-pmc", nargs="+", default=None,
                     help="rocprofv3 --pmc output dirs -> median counters and utilisations (JSON)")
     ap.add_argument("--pmc-pass", default=None, help="print the counters of pass a or b (for --pmc)")
+    ap.add_argument("--sweep-md", default=None, help="FILE: markdown of a --ksweep / --tile-sweep output")
+    ap.add_argument("--profile-md", nargs="+", default=None,
+                    help="NAME TRACE_DIR [PMC_DIR ...] -> markdown summary of the rocprofv3 runs")
     args = ap.parse_args()
     if args.ingest_counters:
         return ingest_counters(args.ingest_counters)
     if args.summarize_pmc:
         return summarize_pmc(args.summarize_pmc)
+    if args.sweep_md:
+        return sweep_md(args.sweep_md)
+    if args.profile_md:
+        name, trace_dir, *pmc_dirs = args.profile_md
+        return profile_md(name, trace_dir, pmc_dirs, args.steps if args.steps != 400 else 200)
     if args.pmc_pass:
         print(" ".join(PMC_PASSES[args.pmc_pass]))
         return 0

@@ -39,7 +39,10 @@ def _configs(fb, route, N):
     return out
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 512, 384), (64, 256, 256), (4160, 3072, 640)])
+# 4160 x 3072 gives more tiles than the persistent grid has workgroups, so workgroups run several
+# tiles; K = 128 and 256 are the shallowest depths (one and two K steps per tile)
+@pytest.mark.parametrize("M,N,K", [(300, 512, 384), (64, 256, 256), (4160, 3072, 640), (4160, 3072, 256),
+                                   (4100, 3072, 128)])
 def test_bs_all_configs_bitwise_equal(fb, oracle, M, N, K):
     x = workload.bs_inputs(M, N, K, 7)
     A, sa, sb = to_dev(x.A), to_dev(x.a_scale_kmajor), to_dev(x.b_scale)
@@ -63,7 +66,7 @@ def test_bs_all_configs_bitwise_equal(fb, oracle, M, N, K):
         assert np.array_equal(got, ref_bits), f"{cfg}: {int((got != ref_bits).sum())} differ"
 
 
-@pytest.mark.parametrize("M,N,K", [(320, 512, 384), (64, 192, 256), (4160, 3072, 640)])
+@pytest.mark.parametrize("M,N,K", [(320, 512, 384), (64, 192, 256), (4160, 3072, 640), (4160, 3072, 256)])
 def test_mx_all_configs_bitwise_equal(fb, oracle, M, N, K):
     y = workload.mx_inputs(M, N, K, 8)
     A = to_dev(y.A)
@@ -93,7 +96,8 @@ def test_invalid_configs_rejected(fb):
                 fb.Config(128, 256, 1, 2, 3, 1, 1, 1), fb.Config(256, 256, 4, 2, 2, 0, 1, 1),  # group_m < 1
                 fb.Config(128, 128, 2, 2, 3, 1, 3, 1), fb.Config(128, 128, 2, 2, 3, 1, 1, 5),
                 fb.Config(256, 128, 4, 2, 3, 1, 1, 1, 1),  # ping-pong needs two stages
-                fb.Config(256, 128, 4, 2, 2, 1, 1, 1, 3),  # no such schedule
+                fb.Config(256, 128, 4, 2, 3, 1, 1, 1, 3),  # no such schedule
+                fb.Config(256, 128, 4, 2, 2, 1, 1, 1, 3),  # no such schedule, nor these stages
                 fb.Config(256, 128, 4, 2, 2, 1, 1, 1, 2)):  # warp-specialised, not with 2 stages
         with pytest.raises(fb.Fp8bsError) as e:
             fb.fp8bs_gemm_with_config(A, sa, Bp, sb, C, cfg)

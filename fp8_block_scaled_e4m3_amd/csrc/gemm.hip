@@ -71,10 +71,12 @@ constexpr int kLdsCapacity = 160 * 1024;
 template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES, int PP>
 struct Tile {
     // PP == 2 (warp-specialised): WM x WN math waves plus four loader waves (one per SIMD:
-    // waves w, w+4, w+8 share a SIMD)
+    // waves w, w+4, w+8 share a SIMD). PP == 3: the same, with part of every finished tile
+    // (but a workgroup's last) held in registers and stored a few pieces per step while the
+    // next tile computes
     static constexpr int kMathWaves = WM * WN;
-    static constexpr int kWaves = PP == 2 ? kMathWaves + 4 : kMathWaves;
-    static constexpr int kLoaders = PP == 2 ? 4 : kWaves;  // waves that issue the loads
+    static constexpr int kWaves = PP >= 2 ? kMathWaves + 4 : kMathWaves;
+    static constexpr int kLoaders = PP >= 2 ? 4 : kWaves;  // waves that issue the loads
     static constexpr int kThreads = kWaves * 64;
     static constexpr int TM = BM / WM;
     static constexpr int TN = BN / WN;
@@ -105,7 +107,12 @@ struct Tile {
     static_assert(STAGES * kStageBytes <= kLdsCapacity, "LDS capacity");
     static_assert(kLoadsPerStep * (STAGES - 1) <= 63, "vmcnt range");
     static_assert(PP != 1 || (STAGES == 2 && kWaves == 8), "ping-pong: two stages, two groups of four waves");
-    static_assert(PP != 2 || kMathWaves == 4 || kMathWaves == 8, "warp-specialised: 4 or 8 math waves");
+    static_assert(PP < 2 || kMathWaves == 4 || kMathWaves == 8, "warp-specialised: 4 or 8 math waves");
+    // C stores per wave and tile (16-byte stores of 16 rows x 64 B), and how many of them PP == 3
+    // holds back: all where a SIMD runs two waves (256 registers each), half where it runs
+    // three (168 each)
+    static constexpr int kStores = SI * SJ / 2;
+    static constexpr int kHold = PP != 3 ? 0 : kWaves <= 8 ? kStores : kStores / 2;
 };
 
 // s_waitcnt for vmcnt <= N and lgkmcnt == 0 (expcnt left unconstrained).
@@ -195,7 +202,7 @@ __device__ __forceinline__ void tile_of(int u, int grid, int tiles_m, int tiles_
 }
 
 template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES, int PP>
-__global__ void __launch_bounds__((WM * WN + (PP == 2 ? 4 : 0)) * 64)
+__global__ void __launch_bounds__((WM * WN + (PP >= 2 ? 4 : 0)) * 64)
 gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
             const uint8_t* __restrict__ B, const void* __restrict__ b_scale,
             uint16_t* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
@@ -214,7 +221,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave % WM;
     const int wn = wave / WM;
-    const int lw = PP == 2 ? wave - T::kMathWaves : wave;  // index among the loading waves
+    const int lw = PP >= 2 ? wave - T::kMathWaves : wave;  // index among the loading waves
     const int KB = K >> 7;
     const int T_total = tiles_m * tiles_n;
     const int grid = gridDim.x;
@@ -349,7 +356,11 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     // The prepared weight rows are ordered so that sub-tiles j and j+1 (j even) hand lane
     // group q output columns 32*(j/2) + 8q .. +7 of the wave's 64-column window: one 16-byte
     // store per lane and pair, sixteen rows x 64 contiguous bytes per store instruction.
-    auto store_tile = [&](int i) {
+    // Stores t = si * SJ/2 + sj/2 of a tile; with hold, the last T::kHold of them are packed
+    // into held[] instead and stored later by trickle().
+    v4i held[T::kHold > 0 ? T::kHold : 1];
+    int held_tile = 0, held_next = T::kHold;  // held stores [held_next, kHold) of held_tile pending
+    auto store_tile = [&](int i, bool hold) {
         int tm, tn;
         tile_of((int)blockIdx.x + i * grid, grid, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
         const int mbase = tm * BM + wm * T::TM + frow;
@@ -375,6 +386,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
             for (int sj = 0; sj < T::SJ; ++sj)
                 asm volatile("" : "+v"(cs[sj]));
         }
+        if constexpr (T::kHold == 0) {
 #pragma unroll
         for (int si = 0; si < T::SI; ++si) {
             const int m = mbase + 16 * si;
@@ -399,6 +411,64 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
 #pragma unroll
             for (int sj = 0; sj < T::SJ; ++sj)
                 acc[si][sj] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+        } else {
+#pragma unroll
+        for (int si = 0; si < T::SI; ++si) {
+            const int m = mbase + 16 * si;
+            uint16_t* crow = C + (size_t)m * N + nbase;
+#pragma unroll
+            for (int sj = 0; sj < T::SJ; sj += 2) {
+                constexpr int kFirstHeld = T::kStores - T::kHold;
+                const int t = si * (T::SJ / 2) + (sj >> 1);
+                v4f lo = acc[si][sj];
+                v4f hi = acc[si][sj + 1];
+                if constexpr (ROUTE == kRoutePT) {
+                    lo = lo * (cs[sj] * rs[si]);
+                    hi = hi * (cs[sj + 1] * rs[si]);
+                }
+                v4i packed;
+                packed.x = (int)pack_bf16x2(lo.x, lo.y);
+                packed.y = (int)pack_bf16x2(lo.z, lo.w);
+                packed.z = (int)pack_bf16x2(hi.x, hi.y);
+                packed.w = (int)pack_bf16x2(hi.z, hi.w);
+                if (T::kHold > 0 && hold && t >= kFirstHeld) {
+                    held[t >= kFirstHeld ? t - kFirstHeld : 0] = packed;
+                } else if (m < M) {
+                    *(v4i*)(crow + 32 * (sj >> 1)) = packed;
+                }
+            }
+#pragma unroll
+            for (int sj = 0; sj < T::SJ; ++sj)
+                acc[si][sj] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+        }
+        if (T::kHold > 0 && hold) {
+            held_tile = i;
+            held_next = 0;
+        }
+    };
+    // store held pieces [held_next, min(held_next + n, kHold))
+    auto trickle = [&](int n) {
+        if constexpr (T::kHold > 0) {
+            if (held_next >= T::kHold)
+                return;
+            int tm, tn;
+            tile_of((int)blockIdx.x + held_tile * grid, grid, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
+            const int mbase = tm * BM + wm * T::TM + frow;
+            const int nbase = tn * BN + wn * T::TN + 8 * (int)q;
+            const int end = min(held_next + n, T::kHold);
+#pragma unroll
+            for (int h = 0; h < T::kHold; ++h) {
+                if (h >= held_next && h < end) {
+                    const int t = T::kStores - T::kHold + h;
+                    const int si = t / (T::SJ / 2), sjp = t % (T::SJ / 2);
+                    const int m = mbase + 16 * si;
+                    if (m < M)
+                        *(v4i*)(C + (size_t)m * N + nbase + 32 * sjp) = held[h];
+                }
+            }
+            held_next = end;
         }
     };
 
@@ -499,7 +569,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     int cp_tile = 0, cp_kb = 0;  // the step being computed
     auto finish_step = [&]() {
         if (++cp_kb == KB) {
-            store_tile(cp_tile);
+            store_tile(cp_tile, false);
             cp_kb = 0;
             ++cp_tile;
         }
@@ -735,15 +805,21 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
             read_head(nxt);
         });
         if (++cp_kb == KB) {
-            store_tile(cp_tile);
+            store_tile(cp_tile, false);
             stores_pending = 1;
             cp_kb = 0;
             ++cp_tile;
         }
     };
-    if constexpr (PP == 2) {
+    if constexpr (PP >= 2) {
         // Warp-specialised: waves kMathWaves.. only move data, the others only compute. Every
         // wave passes one barrier before the first step and one per step.
+        // PP == 3: the math waves hold back kHold of a finished tile's stores (all but a
+        // workgroup's last tile) and issue them a few per step after the next steps' barriers,
+        // so that the tiles the CUs finish at the same moment do not meet as one burst of C
+        // writes in the memory path ahead of the loader waves' next loads. The math waves
+        // issue no loads, so their stores are never waited for inside the loop.
+        const int per_step = (T::kHold + KB - 1) / KB;
         if (wave >= T::kMathWaves) {
             if (total > 0) {
                 static_for<STAGES - 1>([&](auto S) {
@@ -787,8 +863,10 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
                 __builtin_amdgcn_s_barrier();
                 read_head(nxt);
             });
+            if constexpr (T::kHold > 0)
+                trickle(per_step);
             if (++cp_kb == KB) {
-                store_tile(cp_tile);
+                store_tile(cp_tile, T::kHold > 0 && cp_tile + 1 < my_tiles);
                 cp_kb = 0;
                 ++cp_tile;
             }
@@ -810,6 +888,8 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
                     mstep(std::integral_constant<int, 3>{}, s + 3);
             }
         }
+        if constexpr (T::kHold > 0)
+            trickle(T::kHold);  // (nothing is left: the last tile is stored whole)
         __builtin_amdgcn_s_waitcnt(0);
         return;
     }
@@ -908,7 +988,10 @@ static hipError_t launch_tile(const GemmArgs& a, const GemmConfig& c)
     X(13, 256, 128, 4, 2, 3, 2)  \
     X(14, 128, 256, 2, 4, 3, 2)  \
     X(15, 256, 128, 2, 2, 3, 2)  \
-    X(16, 128, 128, 2, 2, 3, 2)
+    X(16, 128, 128, 2, 2, 3, 2)  \
+    X(17, 256, 128, 4, 2, 3, 3)  \
+    X(18, 128, 256, 2, 4, 3, 3)  \
+    X(19, 128, 128, 2, 2, 3, 3)
 
 const VariantInfo* variant_info(int v)
 {

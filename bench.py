@@ -26,6 +26,8 @@ survives a tail of the output whole:
                   no memory traffic
   quantiser, small_m -- compact rows (time, fraction of the HBM peak, parity); the full
                   records go to stderr
+  splitk       -- shapes whose tiles leave CUs idle at deep K: fp8bs_gemm against
+                  fp8bs_gemm_splitk (the library's number of K ranges), parity checked first
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--preroll-ms P] [--no-cpu] [--only NAME]
        python bench.py --profile NAME [--steps K]       (for rocprofv3 runs; also runs a copy
@@ -144,6 +146,31 @@ class Case:
             self.launch = lambda: fn(self.A, self.sa, self.B, self.sb, self.C, stream)
             self.config = {"small_m": 1} if small_mx else \
                 fb.fp8bs_select_config(route_id, self.M, self.N, self.K).as_dict()
+        self.fast_launch(stream, config)
+
+    def fast_launch(self, stream, config=None):
+        """Check every operand once through the binding, then launch with the library call and
+        the device pointers alone: the per-call checks cost a few microseconds of host time,
+        which would set the pace of back-to-back launches of the smallest kernels."""
+        import ctypes
+
+        import fp8_block_scaled_e4m3_amd as fb
+        self.launch()  # the checked call
+        small_mx = self.route == "mx" and self.M % 64 != 0
+        name = {"bs": "fp8bs_gemm", "mx": "fp8mx_gemm_small_m" if small_mx else "fp8mx_gemm",
+                "pt": "fp8pt_gemm"}[self.route] + ("_with_config" if config is not None else "")
+        raw = getattr(fb.lib, name)
+        args = [t.data_ptr() for t in (self.A, self.sa, self.B, self.sb, self.C)] + [self.M, self.N, self.K]
+        if config is not None:
+            args.append(ctypes.byref(config))
+        args.append(stream.cuda_stream)
+        args = tuple(args)
+
+        def launch():
+            st = raw(*args)
+            if st:
+                raise fb.Fp8bsError(name, st)
+        self.launch = launch
 
     @property
     def flops(self) -> int:
@@ -360,10 +387,14 @@ class QuantCase:
         self.A = torch.empty((M, K), dtype=torch.uint8, device="cuda:0")
         if route == "bs":
             self.S = torch.empty((K // 128, M), dtype=torch.float32, device="cuda:0")
-            self.launch = lambda: fb.fp8bs_quantize_act(self.x, self.A, self.S, stream)
+            fb.fp8bs_quantize_act(self.x, self.A, self.S, stream)  # checked once, then launched bare
+            raw = fb.lib.fp8bs_quantize_act
         else:
             self.S = torch.empty((M, K // 32), dtype=torch.uint8, device="cuda:0")
-            self.launch = lambda: fb.fp8mx_quantize_act(self.x, self.A, self.S, stream)
+            fb.fp8mx_quantize_act(self.x, self.A, self.S, stream)
+            raw = fb.lib.fp8mx_quantize_act
+        args = (self.x.data_ptr(), fb.IN_BF16, self.A.data_ptr(), self.S.data_ptr(), M, K, stream.cuda_stream)
+        self.launch = lambda: raw(*args)
         self.config = {"route": route, "M": M, "K": K, "input": "bf16"}
         self.time_launches = lambda steps, warmup, st: Case.time_launches(self, steps, warmup, st)
 
@@ -526,6 +557,40 @@ def ksweep_mode(M: int, N: int, Ks, stream) -> int:
     return 0
 
 
+# shapes whose output tiles leave CUs idle while K is deep (route BS): plain entry against split K
+SPLITK_SHAPES = [(1024, 2048, 7168), (256, 7168, 7168), (128, 7168, 7168), (512, 2048, 4096), (256, 4096, 2048),
+                 (1000, 1536, 7168)]
+
+
+def splitk_rows(stream) -> dict:
+    """fp8bs_gemm against fp8bs_gemm_splitk (the library's number of ranges) on SPLITK_SHAPES:
+    the split output checked against the oracle before timing, both timed as the per-config rows."""
+    import torch
+
+    import fp8_block_scaled_e4m3_amd as fb
+    rows = {}
+    for (M, N, K) in SPLITK_SHAPES:
+        case = Case(f"splitk_{M}x{N}x{K}", 0, stream, shape=(M, N, K))
+        med, _ = case.repeated(stream, preroll_ms=30.0, time_s=0.02)
+        plain = min(med)
+        ws = fb.splitk_workspace(M, N, K, 0, device="cuda:0")
+        splits = fb.fp8bs_splitk_workspace_bytes(M, N, K, 0) // (M * N * 4) if ws is not None else 1
+        case.launch = lambda case=case, ws=ws: fb.fp8bs_gemm_splitk(case.A, case.sa, case.B, case.sb, case.C, ws, 0,
+                                                                    stream)
+        case.launch()
+        torch.cuda.synchronize()
+        par = sampled_parity(case, 8, 8)
+        med, _ = case.repeated(stream, preroll_ms=30.0, time_s=0.02)
+        split = min(med)
+        rows[f"{M}x{N}x{K}"] = dict(splits=int(splits), plain_us=round(plain * 1e6, 2), splitk_us=round(split * 1e6, 2),
+                                    splitk_tflops=round(case.flops / split / 1e12, 1), parity_passed=par["passed"])
+        log(f"[bench] split-K {M}x{N}x{K}: {rows[f'{M}x{N}x{K}']} parity {par}")
+        case.free()
+        del case, ws
+        torch.cuda.empty_cache()
+    return rows
+
+
 # the tiles the sweep tries: (block_m, block_n, waves_m, waves_n, stages, pingpong)
 SWEEP_TILES = [(256, 256, 2, 4, 2, 0), (256, 128, 4, 2, 3, 2), (128, 256, 2, 4, 3, 2), (128, 128, 2, 2, 3, 2),
                (256, 128, 4, 2, 3, 3), (128, 256, 2, 4, 3, 3), (128, 128, 2, 2, 3, 3)]
@@ -556,7 +621,7 @@ def tile_sweep_mode(name: str, stream, group_ms=(2, 4, 8, 16), tiles=None) -> in
                 case.launch = lambda cfg=cfg: fn(case.A, case.sa, case.B, case.sb, case.C, cfg, stream)
                 case.C.fill_(0)
                 try:
-                    case.launch()
+                    case.fast_launch(stream, cfg)
                 except fb.Fp8bsError as e:  # not instantiated for this route
                     log(f"[tile-sweep] {cfg}: {e}")
                     break
@@ -645,8 +710,10 @@ def profile_md(name: str, trace_dir: str, pmc_dirs: list[str], timed: int) -> in
     if not mine:
         print(f"no {match} launches in {trace_dir}", file=sys.stderr)
         return 2
+    def bare(k: str) -> str:  # the kernel name without its parameter list
+        return k.replace("(anonymous namespace)::", "").split("(")[0]
     kname = mine[-1]["Kernel_Name"]
-    short = kname.split("(")[0]
+    short = bare(kname)
     last = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in mine[-timed:]]
     r0 = mine[-1]
     meta = {}
@@ -675,7 +742,7 @@ def profile_md(name: str, trace_dir: str, pmc_dirs: list[str], timed: int) -> in
               "```", "", "## Kernel statistics (all launches, including the warmup ones)", "",
               "| kernel | calls | average ns | min ns | max ns |", "|---|---|---|---|---|"]
     for k, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
-        lines.append(f"| `{k.split('(')[0][:80]}` | {len(v)} | {sum(v) // len(v)} | {min(v)} | {max(v)} |")
+        lines.append(f"| `{bare(k)[:100]}` | {len(v)} | {sum(v) // len(v)} | {min(v)} | {max(v)} |")
     srt = sorted(last)
     lines += ["", f"Average over the last {len(last)} (timed) launches from the kernel trace: "
                   f"**{sum(last) / len(last) / 1e3:.2f} us** (median {srt[len(srt) // 2] / 1e3:.2f} us). The same process "
@@ -775,6 +842,7 @@ def main() -> int:
     ap.add_argument("--ksweep-shape", default="4096,2048")
     ap.add_argument("--ksweep-k", default="1024,2048,3584,7168")
     ap.add_argument("--tile-sweep", default=None)
+    ap.add_argument("--splitk", action="store_true", help="only the split-K rows")
     ap.add_argument("--summarize-pmc", nargs="+", default=None,
                     help="rocprofv3 --pmc output dirs -> median counters and utilisations (JSON)")
     ap.add_argument("--pmc-pass", default=None, help="print the counters of pass a or b (for --pmc)")
@@ -815,6 +883,10 @@ def main() -> int:
     if args.tile_sweep:
         with torch.cuda.stream(stream):
             return tile_sweep_mode(args.tile_sweep, stream)
+    if args.splitk:
+        with torch.cuda.stream(stream):
+            print(json.dumps({"mode": "splitk", "rows": splitk_rows(stream)}), flush=True)
+        return 0
     props = torch.cuda.get_device_properties(0)
     names = [MAIN] + [n for n in workload.CONFIGS if n != MAIN]
     if args.only:
@@ -898,11 +970,13 @@ def main() -> int:
 
         quant = quantiser_rows(stream) if not args.only else {}
         small = small_m_rows(stream, evict) if not args.only else {}
+        splitk = splitk_rows(stream) if not args.only else {}
 
     value = main.flops / wall / 1e12
     achieved = main.flops / ev / 1e12
     parities = [r["parity_passed"] for r in per_config.values()] + [r["parity_passed"] for r in twin.values()] + \
-        [r["parity_passed"] for r in small.values()] + [main_parity["passed"], main_same]
+        [r["parity_passed"] for r in small.values()] + [r["parity_passed"] for r in splitk.values()] + \
+        [main_parity["passed"], main_same]
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -936,6 +1010,7 @@ def main() -> int:
         "quantiser": quant,
         "small_m": {k: {"us": r["us"], "cold_us": r["cold_us"], "cold_frac_hbm": r["cold_frac_hbm"],
                         "parity_passed": r["parity_passed"]} for k, r in small.items()},
+        "splitk": splitk,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "kernel_source_sha256": kernel_source_hash()[:16]},
     }
@@ -958,12 +1033,14 @@ def quantiser_rows(stream) -> dict:
         Aq = torch.empty((Mq, Kq), dtype=torch.uint8, device="cuda:0")
         if qroute == "bs":
             Sq = torch.empty((Kq // 128, Mq), dtype=torch.float32, device="cuda:0")
-            qlaunch = lambda: fb.fp8bs_quantize_act(xq, Aq, Sq, stream)
-            qbytes = Mq * Kq * 3 + Mq * (Kq // 128) * 4
+            fb.fp8bs_quantize_act(xq, Aq, Sq, stream)  # checked once, then launched bare
+            raw, qbytes = fb.lib.fp8bs_quantize_act, Mq * Kq * 3 + Mq * (Kq // 128) * 4
         else:
             Sq = torch.empty((Mq, Kq // 32), dtype=torch.uint8, device="cuda:0")
-            qlaunch = lambda: fb.fp8mx_quantize_act(xq, Aq, Sq, stream)
-            qbytes = Mq * Kq * 3 + Mq * (Kq // 32)
+            fb.fp8mx_quantize_act(xq, Aq, Sq, stream)
+            raw, qbytes = fb.lib.fp8mx_quantize_act, Mq * Kq * 3 + Mq * (Kq // 32)
+        qargs = (xq.data_ptr(), fb.IN_BF16, Aq.data_ptr(), Sq.data_ptr(), Mq, Kq, stream.cuda_stream)
+        qlaunch = lambda: raw(*qargs)
         for _ in range(200):
             qlaunch()
         torch.cuda.synchronize()
@@ -1013,6 +1090,7 @@ def small_m_rows(stream, evict) -> dict:
                 main_cfg = fb.Config(128, 256, 2, 4, 3, 4, 1, 1, 2) if wide else fb.Config(128, 128, 2, 2, 3, 4, 1, 1, 2)
                 for key, c in (("small_m_kernel", forced), ("main_kernel", main_cfg)):
                     dc.launch = lambda dc=dc, c=c: fb.fp8bs_gemm_with_config(dc.A, dc.sa, dc.B, dc.sb, dc.C, c, stream)
+                    dc.fast_launch(stream, c)
                     medm, _ = dc.repeated(stream, preroll_ms=30.0, time_s=0.02)
                     cold_m, _ = dc.cold(stream, evict, reps=9)
                     row.update({f"{key}_us": round(min(medm) * 1e6, 2), f"{key}_cold_us": round(cold_m * 1e6, 2)})

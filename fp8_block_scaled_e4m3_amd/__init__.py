@@ -29,7 +29,7 @@ __all__ = [
     "Config", "ROUTE_BS", "ROUTE_MX", "fp8bs_select_config", "fp8bs_gemm_with_config", "fp8mx_gemm_with_config",
     "fp8bs_mfma_ceiling", "ROUTE_PT", "fp8pt_gemm", "fp8pt_gemm_with_config",
     "IN_F32", "IN_BF16", "fp8bs_quantize_act", "fp8mx_quantize_act", "quantize_bs", "quantize_mx",
-    "fp8mx_gemm_small_m",
+    "fp8mx_gemm_small_m", "fp8bs_splitk_workspace_bytes", "fp8bs_gemm_splitk", "splitk_workspace",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,6 +58,8 @@ SIGNATURES = {
     "fp8mx_gemm_small_m": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp]),
     "fp8mx_quantize_act": (_int, [_vp, _int, _vp, _vp, _int, _int, _vp]),
     "fp8pt_gemm_with_config": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp, _vp]),
+    "fp8bs_splitk_workspace_bytes": (_size, [_int, _int, _int, _int]),
+    "fp8bs_gemm_splitk": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp, _size, _vp]),
 }
 
 ROUTE_BS, ROUTE_MX, ROUTE_PT = 0, 1, 2
@@ -305,6 +307,28 @@ def fp8mx_gemm_small_m(A: torch.Tensor, a_e8m0: torch.Tensor, B_prep: torch.Tens
     _check("fp8mx_gemm_small_m", lib.fp8mx_gemm_small_m(_ptr(A), _ptr(a_e8m0), _ptr(B_prep), _ptr(b_scale_packed),
                                                         _ptr(C), M, N, K, _stream(stream)))
     return C
+
+
+def fp8bs_splitk_workspace_bytes(M: int, N: int, K: int, splits: int = 0) -> int:
+    return lib.fp8bs_splitk_workspace_bytes(M, N, K, splits)
+
+
+def fp8bs_gemm_splitk(A, a_scale, B_prep, b_scale, C, workspace: torch.Tensor | None, splits: int = 0,
+                      stream=None) -> torch.Tensor:
+    """Route BS with K split over `splits` workgroups per output tile (0: the library's choice);
+    workspace: a device tensor of at least fp8bs_splitk_workspace_bytes(M, N, K, splits) bytes
+    (None when the call does not split)."""
+    M, N, K = _gemm_operands("fp8bs_gemm_splitk", "bs", A, a_scale, B_prep, b_scale, C)
+    ws, nbytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
+    _check("fp8bs_gemm_splitk", lib.fp8bs_gemm_splitk(_ptr(A), _ptr(a_scale), _ptr(B_prep), _ptr(b_scale), _ptr(C),
+                                                      M, N, K, splits, ws, nbytes, _stream(stream)))
+    return C
+
+
+def splitk_workspace(M: int, N: int, K: int, splits: int = 0, device="cuda") -> torch.Tensor | None:
+    """A workspace tensor for fp8bs_gemm_splitk (None when the shape does not split)."""
+    n = fp8bs_splitk_workspace_bytes(M, N, K, splits)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
 def fp8bs_select_config(route: int, M: int, N: int, K: int) -> Config:

@@ -18,7 +18,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(HERE, "libfp8bs.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "gemm.hip", "prep.hip", "probe.hip", "quant.hip", "decode.hip"]
+SOURCES = ["api.hip", "gemm.hip", "prep.hip", "probe.hip", "quant.hip", "decode.hip", "splitk.hip"]
 
 # Packed fp32 VALU instructions are disabled on purpose: ordinary float code only.
 FLAGS = [

@@ -193,6 +193,35 @@ fp8bs_config select(int route, int M, int N, int K)
     return square();
 }
 
+// Split K for route BS: the number of equal K ranges per output tile. With the tiles the
+// selector picks (cfg), a shape whose tiles number fewer than the CUs, at K >= 4096, takes the
+// most ranges that keep every work unit within one round of the CUs and at least 8 K blocks deep
+// (K/128 must divide evenly); 1 (no split) otherwise. The second pass and its launch cost about
+// 4 us, which shallower K does not repay (measured, 128 x 128 tiles: 1024 x 2048 x 7168, 2
+// ranges: 26.9 us against 30.7; 128 x 7168 x 7168, 4 ranges: 19.2 against 30.3; 512 x 2048 x
+// 4096, 4 ranges: 17.8 against 19.2; 256 x 4096 x 2048, 2 ranges: 15.0 against 11.4).
+int choose_splits(int M, int N, int K, const fp8bs_config& cfg)
+{
+    const int kCUs = 256;
+    if (cfg.small_m != 0 || K < 4096)
+        return 1;
+    const int v = find_variant(cfg);
+    if (v < 0 || !fp8bs::split_supported(v))
+        return 1;
+    const int tiles = ((M + cfg.block_m - 1) / cfg.block_m) * (N / cfg.block_n);
+    const int KB = K >> 7;
+    int best = 1;
+    for (int s = 2; s <= 8; ++s)
+        if (KB % s == 0 && KB / s >= 8 && (int64_t)tiles * s <= kCUs)
+            best = s;
+    return best;
+}
+
+size_t splitk_bytes(int M, int N, int splits)
+{
+    return splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
 int check_config(int route, const fp8bs_config* c, int N, fp8bs::GemmConfig* out)
 {
     if (!c)
@@ -292,6 +321,7 @@ const char* fp8bs_strerror(int status)
     case FP8BS_E_ALIGN: return "a pointer is not suitably aligned (16 bytes for tensors, 4 for fp32 scales)";
     case FP8BS_E_CONFIG: return "invalid kernel configuration for this shape or route";
     case FP8BS_E_HIP: return "the HIP runtime reported an error while enqueueing work";
+    case FP8BS_E_WORKSPACE: return "the workspace is missing, misaligned or smaller than the call needs";
     default: return "unknown status";
     }
 }
@@ -348,6 +378,44 @@ int fp8bs_gemm_with_config(const void* A, const float* a_scale, const void* B_pr
     if (st != FP8BS_OK)
         return st < 0 ? FP8BS_OK : st;
     return run(fp8bs::kRouteBS, A, a_scale, B_prep, b_scale, C, M, N, K, config, stream);
+}
+
+size_t fp8bs_splitk_workspace_bytes(int M, int N, int K, int splits)
+{
+    if (check_bs_shape(M, N, K) != FP8BS_OK || M == 0)
+        return 0;
+    const fp8bs_config cfg = select(fp8bs::kRouteBS, M, N, K);
+    if (splits <= 0)
+        splits = choose_splits(M, N, K, cfg);
+    return splitk_bytes(M, N, splits);
+}
+
+int fp8bs_gemm_splitk(const void* A, const float* a_scale, const void* B_prep, const float* b_scale, void* C,
+                      int M, int N, int K, int splits, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    int st = check_bs_args(A, a_scale, B_prep, b_scale, C, M, N, K);
+    if (st != FP8BS_OK)
+        return st < 0 ? FP8BS_OK : st;
+    const fp8bs_config cfg = select(fp8bs::kRouteBS, M, N, K);
+    if (splits <= 0)
+        splits = choose_splits(M, N, K, cfg);
+    if (splits > 1 && (cfg.small_m != 0 || !fp8bs::split_supported(find_variant(cfg)) || (K >> 7) % splits != 0 ||
+                       splits > 64))
+        return FP8BS_E_CONFIG;
+    if (splits == 1)
+        return run(fp8bs::kRouteBS, A, a_scale, B_prep, b_scale, C, M, N, K, &cfg, stream);
+    const size_t need = splitk_bytes(M, N, splits);
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+        return FP8BS_E_WORKSPACE;
+    fp8bs::GemmConfig gc;
+    st = check_config(fp8bs::kRouteBS, &cfg, N, &gc);
+    if (st != FP8BS_OK)
+        return st;
+    fp8bs::GemmArgs args{A, a_scale, B_prep, b_scale, C, M, N, K, stream};
+    hipError_t e = fp8bs::launch_gemm_split(args, gc, splits, (float*)workspace);
+    if (e != hipSuccess)
+        return FP8BS_E_HIP;
+    return hip_status(fp8bs::launch_splitk_reduce((const float*)workspace, splits, C, M, N, stream));
 }
 
 size_t fp8mx_packed_scale_bytes(int rows, int K)

@@ -201,12 +201,16 @@ __device__ __forceinline__ void tile_of(int u, int grid, int tiles_m, int tiles_
     tn = r / gm;
 }
 
-template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES, int PP>
+// SPLIT: split K. Each output tile's K blocks are cut into ksplit equal ranges, each computed by
+// its own work unit (unit = split * tiles + tile), which writes its fp32 sums (route PT: before
+// the row and column scales) to partial[split][M][N] instead of C; splitk_reduce_kernel adds the
+// ranges in order and rounds to bf16.
+template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES, int PP, bool SPLIT = false>
 __global__ void __launch_bounds__((WM * WN + (PP >= 2 ? 4 : 0)) * 64)
 gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
             const uint8_t* __restrict__ B, const void* __restrict__ b_scale,
             uint16_t* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
-            int group_m, int xcd_remap)
+            int group_m, int xcd_remap, int ksplit, float* __restrict__ partial)
 {
     using T = Tile<ROUTE, BM, BN, WM, WN, STAGES, PP>;
     // One LDS array per stage: the stage of every read is known at compile time, so the
@@ -222,12 +226,21 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     const int wm = wave % WM;
     const int wn = wave / WM;
     const int lw = PP >= 2 ? wave - T::kMathWaves : wave;  // index among the loading waves
-    const int KB = K >> 7;
     const int T_total = tiles_m * tiles_n;
+    const int n_split = SPLIT ? ksplit : 1;
+    const int KB = (K >> 7) / n_split;  // K blocks per work unit
+    const int U_total = T_total * n_split;
     const int grid = gridDim.x;
-    // number of tiles this workgroup owns, and the length of its step stream
-    const int my_tiles = (int)blockIdx.x < T_total ? (T_total - 1 - (int)blockIdx.x) / grid + 1 : 0;
+    // number of work units (tiles, or tile K ranges) this workgroup owns, and the length of its
+    // step stream
+    const int my_tiles = (int)blockIdx.x < U_total ? (U_total - 1 - (int)blockIdx.x) / grid + 1 : 0;
     const int total = my_tiles * KB;
+    // unit i of this workgroup's list -> output tile (tm, tn) and its K range
+    auto unit_of = [&](int i, int& tm, int& tn, int& split) {
+        const int u = (int)blockIdx.x + i * grid;
+        split = SPLIT ? u / T_total : 0;
+        tile_of(SPLIT ? u - split * T_total : u, grid, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
+    };
 
     const v4i rsA = buffer_desc(A);
     const v4i rsB = buffer_desc(B);
@@ -242,9 +255,11 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     uint32_t voffS[T::kLoadsS > 0 ? T::kLoadsS : 1];  // scale loads: byte offset without the K-block term
     uint32_t kstrS[T::kLoadsS > 0 ? T::kLoadsS : 1];  // bytes per K block of that scale array
     int load_tile = -1;          // tile index (in this workgroup's list) the descriptors describe
+    int load_kb0 = 0;            // its first K block
     auto setup_loads = [&](int i) {
-        int tm, tn;
-        tile_of((int)blockIdx.x + i * grid, grid, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
+        int tm, tn, split;
+        unit_of(i, tm, tn, split);
+        load_kb0 = split * KB;
         const int m0 = tm * BM, n0 = tn * BN;
 #pragma unroll
         for (int g = 0; g < T::kLoadsA; ++g) {
@@ -268,8 +283,8 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
                 }
                 kstrS[g] = (uint32_t)M * 4u;
             } else {
-                if constexpr (ROUTE == kRouteBS) {  // b_scale[nb*KB + kb], fp32
-                    voffS[g] = (uint32_t)((n0 >> 7) + min(lane, (BN + 127) / 128 - 1)) * (uint32_t)KB * 4u;
+                if constexpr (ROUTE == kRouteBS) {  // b_scale[nb*(K/128) + kb], fp32
+                    voffS[g] = (uint32_t)((n0 >> 7) + min(lane, (BN + 127) / 128 - 1)) * (uint32_t)(K >> 7) * 4u;
                     kstrS[g] = 4u;
                 } else {
                     voffS[g] = ((uint32_t)((n0 >> 6) + (u - T::kScaleLoadsA)) * 64u + (uint32_t)lane) * 4u;
@@ -297,7 +312,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
                 ++ld_tile;
             }
         }
-        ld_kbv = kb;
+        ld_kbv = load_kb0 + kb;
     };
     // Load g of the planned group into stage st: A rows, then B rows, then block scales.
     auto lds_addr = [&](lds_u8* p) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)p); };
@@ -361,10 +376,31 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     v4i held[T::kHold > 0 ? T::kHold : 1];
     int held_tile = 0, held_next = T::kHold;  // held stores [held_next, kHold) of held_tile pending
     auto store_tile = [&](int i, bool hold) {
-        int tm, tn;
-        tile_of((int)blockIdx.x + i * grid, grid, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
+        int tm, tn, split;
+        unit_of(i, tm, tn, split);
         const int mbase = tm * BM + wm * T::TM + frow;
         const int nbase = tn * BN + wn * T::TN + 8 * (int)q;
+        if constexpr (SPLIT) {
+            // this K range's fp32 sums, unscaled for route PT: lane group q holds columns
+            // 32*(sj/2) + 8q .. +7 of the wave's window, registers of sub-tile sj then sj + 1
+            float* P = partial + (size_t)split * M * N;
+#pragma unroll
+            for (int si = 0; si < T::SI; ++si) {
+                const int m = mbase + 16 * si;
+                if (m < M) {
+                    float* prow = P + (size_t)m * N + nbase;
+#pragma unroll
+                    for (int sj = 0; sj < T::SJ; sj += 2) {
+                        *(v4f*)(prow + 32 * (sj >> 1)) = acc[si][sj];
+                        *(v4f*)(prow + 32 * (sj >> 1) + 4) = acc[si][sj + 1];
+                    }
+                }
+#pragma unroll
+                for (int sj = 0; sj < T::SJ; ++sj)
+                    acc[si][sj] = v4f{0.f, 0.f, 0.f, 0.f};
+            }
+            return;
+        }
         // Route PT: C = acc * (a_s[m] * b_s[n]), with the row and column scales read here, once
         // per tile, before any store of the tile, and waited for at once (the empty asm uses):
         // no store then sits between a scale load and its use.
@@ -453,8 +489,8 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
         if constexpr (T::kHold > 0) {
             if (held_next >= T::kHold)
                 return;
-            int tm, tn;
-            tile_of((int)blockIdx.x + held_tile * grid, grid, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
+            int tm, tn, split;
+            unit_of(held_tile, tm, tn, split);
             const int mbase = tm * BM + wm * T::TM + frow;
             const int nbase = tn * BN + wn * T::TN + 8 * (int)q;
             const int end = min(held_next + n, T::kHold);
@@ -942,11 +978,11 @@ int device_cus()
     return cus[dev];
 }
 
-template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES, int PP>
-static hipError_t launch_tile(const GemmArgs& a, const GemmConfig& c)
+template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES, int PP, bool SPLIT = false>
+static hipError_t launch_tile(const GemmArgs& a, const GemmConfig& c, int splits = 1, float* partial = nullptr)
 {
     using T = Tile<ROUTE, BM, BN, WM, WN, STAGES, PP>;
-    auto kernel = gemm_kernel<ROUTE, BM, BN, WM, WN, STAGES, PP>;
+    auto kernel = gemm_kernel<ROUTE, BM, BN, WM, WN, STAGES, PP, SPLIT>;
     // workgroups of this kernel that fit on one CU at once (LDS and registers), once per device
     static std::once_flag once[kMaxDevices];
     static int per_cu[kMaxDevices];
@@ -961,13 +997,13 @@ static hipError_t launch_tile(const GemmArgs& a, const GemmConfig& c)
     });
     const int tiles_m = (a.M + BM - 1) / BM;
     const int tiles_n = a.N / BN;
-    const int T_total = tiles_m * tiles_n;
+    const int units = tiles_m * tiles_n * (SPLIT ? splits : 1);
     int grid = device_cus() * per_cu[dev];
-    if (c.persistent == 0 || grid > T_total)
-        grid = T_total;
+    if (c.persistent == 0 || grid > units)
+        grid = units;
     return launch_kernel(kernel, dim3(grid), dim3(T::kThreads), a.stream, (const uint8_t*)a.A, a.a_scale,
                          (const uint8_t*)a.B, a.b_scale, (uint16_t*)a.C, a.M, a.N, a.K, tiles_m, tiles_n,
-                         c.group_m > 0 ? c.group_m : 1, c.xcd_remap);
+                         c.group_m > 0 ? c.group_m : 1, c.xcd_remap, SPLIT ? splits : 1, partial);
 }
 
 // Instantiated shapes: {BM, BN, WM, WN, STAGES, ping-pong}. Index = GemmConfig::variant.
@@ -1040,6 +1076,29 @@ bool variant_supports(int route, int v)
     if (route == kRoutePT)
         return true;
     return TM % 64 == 0 && TN % 64 == 0 && vi->stages * (vi->block_m * 132 + vi->block_n * 132) <= kLdsCapacity;
+}
+
+// Route BS with K split `splits` ways, fp32 sums into partial[splits][M][N]: the
+// warp-specialised tiles only (the selector's choice wherever a shape's tiles leave CUs idle).
+bool split_supported(int v)
+{
+    return v == 13 || v == 14 || v == 16;
+}
+
+hipError_t launch_gemm_split(const GemmArgs& a, const GemmConfig& c, int splits, float* partial)
+{
+    if (splits < 1 || (a.K >> 7) % splits != 0 || !partial)
+        return hipErrorInvalidValue;
+    switch (c.variant) {
+    case 13:
+        return launch_tile<kRouteBS, 256, 128, 4, 2, 3, 2, true>(a, c, splits, partial);
+    case 14:
+        return launch_tile<kRouteBS, 128, 256, 2, 4, 3, 2, true>(a, c, splits, partial);
+    case 16:
+        return launch_tile<kRouteBS, 128, 128, 2, 2, 3, 2, true>(a, c, splits, partial);
+    default:
+        return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_gemm(int route, const GemmArgs& a, const GemmConfig& c)

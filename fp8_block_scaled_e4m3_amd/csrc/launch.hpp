@@ -55,6 +55,12 @@ const VariantInfo* variant_info(int v);
 int device_cus();
 bool variant_supports(int route, int v);
 hipError_t launch_gemm(int route, const GemmArgs& a, const GemmConfig& c);
+// Split K (route BS): the tile GEMM writes fp32 sums of each of `splits` equal K ranges to
+// partial[splits][M][N] (K/128 % splits == 0; variants with split_supported()), then
+// launch_splitk_reduce adds them in range order and rounds to bf16 C.
+bool split_supported(int variant);
+hipError_t launch_gemm_split(const GemmArgs& a, const GemmConfig& c, int splits, float* partial);
+hipError_t launch_splitk_reduce(const float* partial, int splits, void* C, int M, int N, hipStream_t stream);
 hipError_t launch_mfma_ceiling(const void* A, const void* B_prep, int M, int N, int K, int iters, float* sink,
                                int sink_len, long long* flops, hipStream_t stream);
 hipError_t launch_prep_weights(const void* B, void* B_prep, int N, int K, hipStream_t stream);

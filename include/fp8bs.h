@@ -56,7 +56,8 @@ typedef enum {
     FP8BS_E_SHAPE = 2,   /* M, N or K violates the route's constraints                   */
     FP8BS_E_ALIGN = 3,   /* a pointer is not 16-byte aligned                             */
     FP8BS_E_CONFIG = 4,  /* an explicit kernel configuration is invalid for the shape    */
-    FP8BS_E_HIP = 5      /* the HIP runtime reported an error when enqueueing the work   */
+    FP8BS_E_HIP = 5,     /* the HIP runtime reported an error when enqueueing the work   */
+    FP8BS_E_WORKSPACE = 6 /* a workspace is missing, misaligned or too small             */
 } fp8bs_status;
 
 /* Version of this ABI (major * 10000 + minor * 100 + patch). */
@@ -124,6 +125,33 @@ int fp8mx_quantize_act(const void *x, int x_dtype, void *A_codes, void *a_e8m0, 
  * last row tile masks its stores. Results are bitwise deterministic run to run. */
 int fp8bs_gemm(const void *A, const float *a_scale, const void *B_prep, const float *b_scale,
                void *C, int M, int N, int K, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Route BS with split K: for shapes whose output tiles are too few to occupy the CUs while K
+ * is deep (a grid of few workgroups is bound by each tile's K loop: page "Flydsl Fp8 Blockscale
+ * Gemm", Bottleneck diagnosis), each tile's 128-wide K blocks are cut into `splits` equal ranges
+ * computed by separate workgroups; their fp32 sums go to a caller-provided workspace and a
+ * second kernel adds them in range order and rounds once to bf16. The result is deterministic
+ * and meets the same bar as fp8bs_gemm; its last bits can differ from fp8bs_gemm's (the fp32
+ * sums are grouped by range), and are those of fp8bs_gemm with splits == 1.
+ * ------------------------------------------------------------------------------------------ */
+
+/* Workspace bytes fp8bs_gemm_splitk needs: splits x M x N x 4 (0 when it does not split).
+ * splits <= 0 asks for the library's choice for the shape (the same choice fp8bs_gemm_splitk
+ * makes with splits <= 0). 0 as well for shapes route BS rejects. */
+size_t fp8bs_splitk_workspace_bytes(int M, int N, int K, int splits);
+
+/* fp8bs_gemm with K split `splits` ways (splits <= 0: the library's choice; 1: exactly
+ * fp8bs_gemm, no workspace used). Operands, layouts and constraints as fp8bs_gemm; in addition
+ * (K/128) % splits == 0, splits <= 64, and the shape's tiles must be ones the split kernels
+ * have (the warp-specialised tiles the selector takes for grids smaller than the CUs), else
+ * FP8BS_E_CONFIG. workspace: device memory of at least fp8bs_splitk_workspace_bytes(M, N, K,
+ * splits) bytes, 256-byte aligned, owned by the caller and overwritten; FP8BS_E_WORKSPACE if
+ * it is NULL, misaligned or too small (only checked when the call splits). Two kernels are
+ * enqueued on `stream`; the workspace must not be used by other work until they finish. */
+int fp8bs_gemm_splitk(const void *A, const float *a_scale, const void *B_prep, const float *b_scale,
+                      void *C, int M, int N, int K, int splits, void *workspace, size_t workspace_bytes,
+                      hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
  * Route MX.

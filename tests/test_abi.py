@@ -286,3 +286,25 @@ def test_contract_calls_are_exported(fb):
         assert hasattr(handle, name) and name in declared, f"{want}: {name} not exported"
     assert fb.fp8bs_prep_bytes(256, 512) == fb.fp8bs_prep_weight_bytes(256, 512) == 256 * 512
     assert fb.fp8mx_scale_bytes(128, 512) == fb.fp8mx_packed_scale_bytes(128, 512) == 128 * 16
+
+
+def test_splitk_sizes_and_host_rejections(fb):
+    """The library's split choice and its workspace size; rejections before any launch."""
+    assert fb.fp8bs_splitk_workspace_bytes(1024, 2048, 7168, 0) == 2 * 1024 * 2048 * 4  # 128 tiles x 2 ranges
+    assert fb.fp8bs_splitk_workspace_bytes(1024, 2048, 7168, 1) == 0
+    assert fb.fp8bs_splitk_workspace_bytes(1024, 2048, 7168, 4) == 4 * 1024 * 2048 * 4
+    assert fb.fp8bs_splitk_workspace_bytes(4096, 2048, 7168, 0) == 0  # 256 tiles fill the CUs
+    assert fb.fp8bs_splitk_workspace_bytes(100, 100, 128, 0) == 0     # a shape route BS rejects
+    assert fb.fp8bs_splitk_workspace_bytes(256, 4096, 2048, 0) == 0   # too shallow to repay the second pass
+    assert fb.fp8bs_splitk_workspace_bytes(128, 7168, 7168, 0) == 4 * 128 * 7168 * 4
+    p = 0x10000
+    L = fb.lib
+    assert L.fp8bs_gemm_splitk(p, p, p, p, p, 1024, 2048, 7168, 0, None, 0, None) == 6
+    assert L.fp8bs_gemm_splitk(p, p, p, p, p, 1024, 2048, 7168, 0, p + 16, 1 << 30, None) == 6  # misaligned
+    assert L.fp8bs_gemm_splitk(p, p, p, p, p, 1024, 2048, 7168, 0, p, 2 * 1024 * 2048 * 4 - 1, None) == 6
+    assert L.fp8bs_gemm_splitk(p, p, p, p, p, 1024, 2048, 7168, 3, p, 1 << 30, None) == 4  # 56 % 3
+    assert L.fp8bs_gemm_splitk(p, p, p, p, p, 1024, 2048, 7168, 65, p, 1 << 30, None) == 4
+    assert L.fp8bs_gemm_splitk(p, p, p, p, p, 1024, 100, 7168, 2, p, 1 << 30, None) == 2
+    assert L.fp8bs_gemm_splitk(None, p, p, p, p, 1024, 2048, 7168, 2, p, 1 << 30, None) == 1
+    assert L.fp8bs_gemm_splitk(p, p, p, p, p, 0, 2048, 7168, 2, None, 0, None) == 0
+    assert fb.fp8bs_strerror(6).startswith("the workspace")

@@ -30,6 +30,7 @@ __all__ = [
     "fp8bs_mfma_ceiling", "ROUTE_PT", "fp8pt_gemm", "fp8pt_gemm_with_config",
     "IN_F32", "IN_BF16", "fp8bs_quantize_act", "fp8mx_quantize_act", "quantize_bs", "quantize_mx",
     "fp8mx_gemm_small_m", "fp8bs_splitk_workspace_bytes", "fp8bs_gemm_splitk", "splitk_workspace",
+    "fp8bs_gemm_splitk_noalloc", "SPLITK_SCRATCH_BYTES",
 ]
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -60,6 +61,7 @@ SIGNATURES = {
     "fp8pt_gemm_with_config": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp, _vp]),
     "fp8bs_splitk_workspace_bytes": (_size, [_int, _int, _int, _int]),
     "fp8bs_gemm_splitk": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp, _size, _vp]),
+    "fp8bs_gemm_splitk_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _vp]),
 }
 
 ROUTE_BS, ROUTE_MX, ROUTE_PT = 0, 1, 2
@@ -322,6 +324,19 @@ def fp8bs_gemm_splitk(A, a_scale, B_prep, b_scale, C, workspace: torch.Tensor | 
     ws, nbytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
     _check("fp8bs_gemm_splitk", lib.fp8bs_gemm_splitk(_ptr(A), _ptr(a_scale), _ptr(B_prep), _ptr(b_scale), _ptr(C),
                                                       M, N, K, splits, ws, nbytes, _stream(stream)))
+    return C
+
+
+SPLITK_SCRATCH_BYTES = 32 << 20  # FP8BS_SPLITK_SCRATCH_BYTES of include/fp8bs.h
+
+
+def fp8bs_gemm_splitk_noalloc(A, a_scale, B_prep, b_scale, C, splits: int = 0, stream=None) -> torch.Tensor:
+    """fp8bs_gemm_splitk with the library's static scratch instead of a workspace (nothing is
+    allocated; calls that overlap on one GPU race)."""
+    M, N, K = _gemm_operands("fp8bs_gemm_splitk_noalloc", "bs", A, a_scale, B_prep, b_scale, C)
+    _check("fp8bs_gemm_splitk_noalloc",
+           lib.fp8bs_gemm_splitk_noalloc(_ptr(A), _ptr(a_scale), _ptr(B_prep), _ptr(b_scale), _ptr(C), M, N, K,
+                                         splits, _stream(stream)))
     return C
 
 

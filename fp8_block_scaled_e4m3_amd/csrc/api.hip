@@ -390,8 +390,14 @@ size_t fp8bs_splitk_workspace_bytes(int M, int N, int K, int splits)
     return splitk_bytes(M, N, splits);
 }
 
-int fp8bs_gemm_splitk(const void* A, const float* a_scale, const void* B_prep, const float* b_scale, void* C,
-                      int M, int N, int K, int splits, void* workspace, size_t workspace_bytes, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+// fp8bs_gemm_splitk's work with workspace ws of ws_bytes (ws may be null when nothing splits);
+// `noalloc`: ws is the library's scratch, and a call that needs more returns FP8BS_E_WORKSPACE
+int splitk_run(const void* A, const float* a_scale, const void* B_prep, const float* b_scale, void* C, int M,
+               int N, int K, int splits, void* ws, size_t ws_bytes, bool noalloc, hipStream_t stream)
 {
     int st = check_bs_args(A, a_scale, B_prep, b_scale, C, M, N, K);
     if (st != FP8BS_OK)
@@ -405,17 +411,41 @@ int fp8bs_gemm_splitk(const void* A, const float* a_scale, const void* B_prep, c
     if (splits == 1)
         return run(fp8bs::kRouteBS, A, a_scale, B_prep, b_scale, C, M, N, K, &cfg, stream);
     const size_t need = splitk_bytes(M, N, splits);
-    if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+    if (noalloc) {
+        if (need > ws_bytes)
+            return FP8BS_E_WORKSPACE;
+        ws = fp8bs::splitk_scratch();
+        if (!ws)
+            return FP8BS_E_HIP;
+    }
+    if (!ws || !aligned(ws, 256) || ws_bytes < need)
         return FP8BS_E_WORKSPACE;
     fp8bs::GemmConfig gc;
     st = check_config(fp8bs::kRouteBS, &cfg, N, &gc);
     if (st != FP8BS_OK)
         return st;
     fp8bs::GemmArgs args{A, a_scale, B_prep, b_scale, C, M, N, K, stream};
-    hipError_t e = fp8bs::launch_gemm_split(args, gc, splits, (float*)workspace);
+    hipError_t e = fp8bs::launch_gemm_split(args, gc, splits, (float*)ws);
     if (e != hipSuccess)
         return FP8BS_E_HIP;
-    return hip_status(fp8bs::launch_splitk_reduce((const float*)workspace, splits, C, M, N, stream));
+    return hip_status(fp8bs::launch_splitk_reduce((const float*)ws, splits, C, M, N, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int fp8bs_gemm_splitk(const void* A, const float* a_scale, const void* B_prep, const float* b_scale, void* C,
+                      int M, int N, int K, int splits, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return splitk_run(A, a_scale, B_prep, b_scale, C, M, N, K, splits, workspace, workspace_bytes, false, stream);
+}
+
+int fp8bs_gemm_splitk_noalloc(const void* A, const float* a_scale, const void* B_prep, const float* b_scale,
+                              void* C, int M, int N, int K, int splits, hipStream_t stream)
+{
+    return splitk_run(A, a_scale, B_prep, b_scale, C, M, N, K, splits, nullptr, fp8bs::kSplitkScratchBytes, true,
+                      stream);
 }
 
 size_t fp8mx_packed_scale_bytes(int rows, int K)

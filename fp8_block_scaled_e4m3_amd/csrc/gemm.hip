@@ -960,7 +960,6 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
 
 // Compute units of each device, read once per device (std::call_once: the first calls may come
 // from several host threads at once).
-constexpr int kMaxDevices = 64;
 
 int device_cus()
 {

@@ -8,6 +8,9 @@
 
 namespace fp8bs {
 
+// Per-device host caches hold this many devices.
+constexpr int kMaxDevices = 64;
+
 // Enqueue kernel<<<grid, block, 0, stream>>>(args...) and return the status of this launch
 // alone (hipLaunchKernel's own return value): an error that earlier, unrelated work left
 // pending in the runtime is neither reported as this launch's failure nor cleared.
@@ -61,6 +64,10 @@ hipError_t launch_gemm(int route, const GemmArgs& a, const GemmConfig& c);
 bool split_supported(int variant);
 hipError_t launch_gemm_split(const GemmArgs& a, const GemmConfig& c, int splits, float* partial);
 hipError_t launch_splitk_reduce(const float* partial, int splits, void* C, int M, int N, hipStream_t stream);
+// The library's static split-K scratch on the current device (kSplitkScratchBytes, 256-byte
+// aligned): its device address, looked up once per device; nullptr if the lookup failed.
+constexpr size_t kSplitkScratchBytes = (size_t)32 << 20;
+void* splitk_scratch();
 hipError_t launch_mfma_ceiling(const void* A, const void* B_prep, int M, int N, int K, int iters, float* sink,
                                int sink_len, long long* flops, hipStream_t stream);
 hipError_t launch_prep_weights(const void* B, void* B_prep, int N, int K, hipStream_t stream);

@@ -9,7 +9,29 @@
 #include "device.hpp"
 #include "launch.hpp"
 
+#include <mutex>
+
 namespace fp8bs {
+
+// Scratch for the split-K partial tiles of fp8bs_gemm_splitk_noalloc, for callers that cannot
+// allocate: one copy per GPU, held until the process ends. Host code never uses this name as an
+// address (on the host it is a stand-in, not device memory): splitk_scratch() looks up the
+// device address once per device and every launch takes that pointer.
+static __device__ __align__(256) uint8_t scratch[kSplitkScratchBytes];
+
+void* splitk_scratch()
+{
+    static std::once_flag once[kMaxDevices];
+    static void* ptr[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return nullptr;
+    std::call_once(once[dev], [dev] {  // with device `dev` current
+        void* p = nullptr;
+        ptr[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess ? p : nullptr;
+    });
+    return ptr[dev];
+}
 
 namespace {
 

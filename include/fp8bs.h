@@ -153,6 +153,19 @@ int fp8bs_gemm_splitk(const void *A, const float *a_scale, const void *B_prep, c
                       void *C, int M, int N, int K, int splits, void *workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
+/* fp8bs_gemm_splitk without a workspace argument, for callers that cannot allocate (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation). The partial tiles
+ * go to the library's own scratch: a static device array of FP8BS_SPLITK_SCRATCH_BYTES on each
+ * GPU it runs on, held until the process ends. The call allocates and frees nothing. A call
+ * whose partial tiles need more (fp8bs_splitk_workspace_bytes(M, N, K, splits) above the
+ * limit) returns FP8BS_E_WORKSPACE and launches nothing. Every call on one GPU shares that
+ * array and leaves the last call's partial tiles in it: calls that overlap on one GPU (from
+ * different streams or host threads) race, and the caller must order them. Other arguments,
+ * constraints and results as fp8bs_gemm_splitk, whose kernels this call runs. */
+#define FP8BS_SPLITK_SCRATCH_BYTES ((size_t)32 << 20)
+int fp8bs_gemm_splitk_noalloc(const void *A, const float *a_scale, const void *B_prep, const float *b_scale,
+                              void *C, int M, int N, int K, int splits, hipStream_t stream);
+
 /* ------------------------------------------------------------------------------------------
  * Route MX.
  * ------------------------------------------------------------------------------------------ */

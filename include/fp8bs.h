@@ -27,7 +27,8 @@
  *
  * Conventions shared by every entry point:
  *   - Pointers are device pointers unless stated otherwise; the caller owns every buffer.
- *     The library never allocates, frees or keeps per-call state.
+ *     No call allocates, frees or keeps per-call state (fp8bs_gemm_splitk_noalloc uses a fixed
+ *     static device array instead of a workspace).
  *   - Work is enqueued asynchronously on `stream` (0 = the null stream). No call synchronises
  *     the host, so calls may be captured into a HIP graph.
  *   - Every call returns an fp8bs_status. Pointer, shape and alignment checks run on the host

@@ -592,8 +592,7 @@ def splitk_rows(stream) -> dict:
 
 
 # the tiles the sweep tries: (block_m, block_n, waves_m, waves_n, stages, pingpong)
-SWEEP_TILES = [(256, 256, 2, 4, 2, 0), (256, 128, 4, 2, 3, 2), (128, 256, 2, 4, 3, 2), (128, 128, 2, 2, 3, 2),
-               (256, 128, 4, 2, 3, 3), (128, 256, 2, 4, 3, 3), (128, 128, 2, 2, 3, 3)]
+SWEEP_TILES = [(256, 256, 2, 4, 2, 0), (256, 128, 4, 2, 3, 2), (128, 256, 2, 4, 3, 2), (128, 128, 2, 2, 3, 2)]
 
 
 def tile_sweep_mode(name: str, stream, group_ms=(2, 4, 8, 16), tiles=None) -> int:

@@ -37,11 +37,13 @@ __device__ __forceinline__ v4f mfma_f8(const v8i& a, const v8i& b, const v4f& c)
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, kFmtE4M3, kFmtE4M3, 0, 0, 0, 0);
 }
 
-// Two fp32 -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even).
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair, round to nearest even: one v_cvt_pk_bf16_f32 (converted as a
+// pair; two separate conversions cost a shift and an or besides).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    __bf16 a = (__bf16)lo;
-    __bf16 b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v2f{lo, hi}, v2bf));
 }
 
 // Row order of the prepared weight buffer inside each 64-row window: prepared row

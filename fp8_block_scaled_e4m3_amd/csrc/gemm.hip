@@ -26,15 +26,19 @@
 //    (swap-AB), so every lane owns four consecutive columns of one output row and stores
 //    8 contiguous bytes (page "aiter PR #6370", "Why it is faster", first bullet). Of the two
 //    operands the one with fewer fragments per wave is held in registers for the whole step
-//    and the other streams through a two-deep register ring.
-//  * One barrier per step, placed after the last matrix instruction of the step is issued:
-//    the wave then reads the first fragments of the next step while its last instructions
-//    and the promotes still run.
+//    and the other streams through a two-deep register ring; one barrier per step, after the
+//    step's last matrix instruction, after which the wave reads the next step's first
+//    fragments while its last instructions and promotes still run.
 //  * Schedules (config field `pingpong`): 0, every wave loads and computes; 1, ping-pong (the
 //    two halves of the workgroup alternate memory and matrix phases); 2, warp-specialised:
 //    WM x WN math waves that only read LDS and run matrix instructions, plus four loader waves
 //    (one per SIMD) that only issue the global -> LDS loads, so the load-issue stalls of the
-//    texture path never hold up a wave that has matrix work to issue.
+//    texture path never hold up a wave that has matrix work to issue. With 64 x 64 per wave
+//    the math waves of schedule 2 hold all eight fragments of a step in registers: the barrier
+//    sits after the step's first row of instructions, and each fragment of the next step is
+//    read as soon as its register falls free, a row or more ahead of its use. Every LDS address
+//    is then a per-lane base plus an immediate offset, which leaves the vector ALU to the
+//    promote (each vector instruction taken out of the loop shortened it measurably).
 //  * Tiles are handed out so that the workgroups running at the same time on one XCD (each
 //    XCD has its own L2) work on neighbouring tiles (page "Flydsl Fp8 Blockscale Gemm",
 //    Mechanism B: XCD-aware rasterisation).
@@ -52,6 +56,10 @@
 namespace fp8bs {
 
 __device__ __forceinline__ uint32_t swz(uint32_t row) { return (row >> 1) & 7u; }
+
+// The kernel's lambdas are always inlined: a lambda left as a call keeps its captures in
+// scratch memory (the optimiser's inlining budget runs out on the larger tiles otherwise).
+#define FP8BS_INLINE __attribute__((always_inline))
 
 // The software promote acc + p * s, one fused multiply-add per component (one rounding), spelled
 // out so that every schedule rounds the same way whatever the optimiser hoists or shares.
@@ -71,9 +79,7 @@ constexpr int kLdsCapacity = 160 * 1024;
 template <int ROUTE, int BM, int BN, int WM, int WN, int STAGES, int PP>
 struct Tile {
     // PP == 2 (warp-specialised): WM x WN math waves plus four loader waves (one per SIMD:
-    // waves w, w+4, w+8 share a SIMD). PP == 3: the same, with part of every finished tile
-    // (but a workgroup's last) held in registers and stored a few pieces per step while the
-    // next tile computes
+    // waves w, w+4, w+8 share a SIMD)
     static constexpr int kMathWaves = WM * WN;
     static constexpr int kWaves = PP >= 2 ? kMathWaves + 4 : kMathWaves;
     static constexpr int kLoaders = PP >= 2 ? 4 : kWaves;  // waves that issue the loads
@@ -108,11 +114,7 @@ struct Tile {
     static_assert(kLoadsPerStep * (STAGES - 1) <= 63, "vmcnt range");
     static_assert(PP != 1 || (STAGES == 2 && kWaves == 8), "ping-pong: two stages, two groups of four waves");
     static_assert(PP < 2 || kMathWaves == 4 || kMathWaves == 8, "warp-specialised: 4 or 8 math waves");
-    // C stores per wave and tile (16-byte stores of 16 rows x 64 B), and how many of them PP == 3
-    // holds back: all where a SIMD runs two waves (256 registers each), half where it runs
-    // three (168 each)
-    static constexpr int kStores = SI * SJ / 2;
-    static constexpr int kHold = PP != 3 ? 0 : kWaves <= 8 ? kStores : kStores / 2;
+    static_assert(PP <= 2, "schedules 0 to 2");
 };
 
 // s_waitcnt for vmcnt <= N and lgkmcnt == 0 (expcnt left unconstrained).
@@ -236,7 +238,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     const int my_tiles = (int)blockIdx.x < U_total ? (U_total - 1 - (int)blockIdx.x) / grid + 1 : 0;
     const int total = my_tiles * KB;
     // unit i of this workgroup's list -> output tile (tm, tn) and its K range
-    auto unit_of = [&](int i, int& tm, int& tn, int& split) {
+    auto unit_of = [&](int i, int& tm, int& tn, int& split) FP8BS_INLINE {
         const int u = (int)blockIdx.x + i * grid;
         split = SPLIT ? u / T_total : 0;
         tile_of(SPLIT ? u - split * T_total : u, grid, tiles_m, tiles_n, group_m, xcd_remap, tm, tn);
@@ -256,7 +258,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     uint32_t kstrS[T::kLoadsS > 0 ? T::kLoadsS : 1];  // bytes per K block of that scale array
     int load_tile = -1;          // tile index (in this workgroup's list) the descriptors describe
     int load_kb0 = 0;            // its first K block
-    auto setup_loads = [&](int i) {
+    auto setup_loads = [&](int i) FP8BS_INLINE {
         int tm, tn, split;
         unit_of(i, tm, tn, split);
         load_kb0 = split * KB;
@@ -301,7 +303,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     // a compile-time constant.
     int ld_tile = 0, ld_kb = 0;
     int ld_kbv = 0;  // K block of the planned group
-    auto plan_loads = [&](bool real) {
+    auto plan_loads = [&](bool real) FP8BS_INLINE {
         int kb = 0;
         if (real) {
             if (ld_tile != load_tile)
@@ -316,7 +318,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     };
     // Load g of the planned group into stage st: A rows, then B rows, then block scales.
     auto lds_addr = [&](lds_u8* p) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)p); };
-    auto issue_load = [&](auto G, lds_u8* st) {
+    auto issue_load = [&](auto G, lds_u8* st) FP8BS_INLINE {
         constexpr int g = decltype(G)::value;
         const int koff = __builtin_amdgcn_readfirstlane(ld_kbv * 128);
         if constexpr (g < T::kLoadsA) {
@@ -335,7 +337,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
             lds_dma<4>(rs, lds_addr(dst), (int)voffS[gs], soff);
         }
     };
-    auto issue_group = [&](lds_u8* st) {
+    auto issue_group = [&](lds_u8* st) FP8BS_INLINE {
         static_for<T::kLoadsPerStep>([&](auto G) { issue_load(G, st); });
     };
 
@@ -356,26 +358,12 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
         const v4i hi = *(const v4i*)(base + c_hi);
         return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     };
-    // The same read, kept in place: the optimiser may not move it above the preceding
-    // instructions (it would otherwise hoist every streamed read of a step to its start and
-    // hold them all in registers).
-    auto frag_here = [&](const uint8_t* base) -> v8i {
-        uint32_t lo_off = c_lo, hi_off = c_hi;
-        asm volatile("" : "+v"(lo_off), "+v"(hi_off));
-        const v4i lo = *(const v4i*)(base + lo_off);
-        const v4i hi = *(const v4i*)(base + hi_off);
-        return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    };
 
     // ---- epilogue: fp32 -> bf16 (nearest even) -------------------------------------------
     // The prepared weight rows are ordered so that sub-tiles j and j+1 (j even) hand lane
     // group q output columns 32*(j/2) + 8q .. +7 of the wave's 64-column window: one 16-byte
     // store per lane and pair, sixteen rows x 64 contiguous bytes per store instruction.
-    // Stores t = si * SJ/2 + sj/2 of a tile; with hold, the last T::kHold of them are packed
-    // into held[] instead and stored later by trickle().
-    v4i held[T::kHold > 0 ? T::kHold : 1];
-    int held_tile = 0, held_next = T::kHold;  // held stores [held_next, kHold) of held_tile pending
-    auto store_tile = [&](int i, bool hold) {
+    auto store_tile = [&](int i) FP8BS_INLINE {
         int tm, tn, split;
         unit_of(i, tm, tn, split);
         const int mbase = tm * BM + wm * T::TM + frow;
@@ -422,7 +410,6 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
             for (int sj = 0; sj < T::SJ; ++sj)
                 asm volatile("" : "+v"(cs[sj]));
         }
-        if constexpr (T::kHold == 0) {
 #pragma unroll
         for (int si = 0; si < T::SI; ++si) {
             const int m = mbase + 16 * si;
@@ -447,64 +434,6 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
 #pragma unroll
             for (int sj = 0; sj < T::SJ; ++sj)
                 acc[si][sj] = v4f{0.f, 0.f, 0.f, 0.f};
-        }
-        } else {
-#pragma unroll
-        for (int si = 0; si < T::SI; ++si) {
-            const int m = mbase + 16 * si;
-            uint16_t* crow = C + (size_t)m * N + nbase;
-#pragma unroll
-            for (int sj = 0; sj < T::SJ; sj += 2) {
-                constexpr int kFirstHeld = T::kStores - T::kHold;
-                const int t = si * (T::SJ / 2) + (sj >> 1);
-                v4f lo = acc[si][sj];
-                v4f hi = acc[si][sj + 1];
-                if constexpr (ROUTE == kRoutePT) {
-                    lo = lo * (cs[sj] * rs[si]);
-                    hi = hi * (cs[sj + 1] * rs[si]);
-                }
-                v4i packed;
-                packed.x = (int)pack_bf16x2(lo.x, lo.y);
-                packed.y = (int)pack_bf16x2(lo.z, lo.w);
-                packed.z = (int)pack_bf16x2(hi.x, hi.y);
-                packed.w = (int)pack_bf16x2(hi.z, hi.w);
-                if (T::kHold > 0 && hold && t >= kFirstHeld) {
-                    held[t >= kFirstHeld ? t - kFirstHeld : 0] = packed;
-                } else if (m < M) {
-                    *(v4i*)(crow + 32 * (sj >> 1)) = packed;
-                }
-            }
-#pragma unroll
-            for (int sj = 0; sj < T::SJ; ++sj)
-                acc[si][sj] = v4f{0.f, 0.f, 0.f, 0.f};
-        }
-        }
-        if (T::kHold > 0 && hold) {
-            held_tile = i;
-            held_next = 0;
-        }
-    };
-    // store held pieces [held_next, min(held_next + n, kHold))
-    auto trickle = [&](int n) {
-        if constexpr (T::kHold > 0) {
-            if (held_next >= T::kHold)
-                return;
-            int tm, tn, split;
-            unit_of(held_tile, tm, tn, split);
-            const int mbase = tm * BM + wm * T::TM + frow;
-            const int nbase = tn * BN + wn * T::TN + 8 * (int)q;
-            const int end = min(held_next + n, T::kHold);
-#pragma unroll
-            for (int h = 0; h < T::kHold; ++h) {
-                if (h >= held_next && h < end) {
-                    const int t = T::kStores - T::kHold + h;
-                    const int si = t / (T::SJ / 2), sjp = t % (T::SJ / 2);
-                    const int m = mbase + 16 * si;
-                    if (m < M)
-                        *(v4i*)(C + (size_t)m * N + nbase + 32 * sjp) = held[h];
-                }
-            }
-            held_next = end;
         }
     };
 
@@ -531,7 +460,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
         int ia[GA];                                // MX: packed activation scale dwords
         int ib[GB];                                // MX: packed weight scale dwords
     };
-    auto read_all = [&](const uint8_t* st, Frags& F) {
+    auto read_all = [&](const uint8_t* st, Frags& F) FP8BS_INLINE {
         const uint8_t* sA = st + (wm * T::TM) * 128;
         const uint8_t* sB = st + T::kABytes + (wn * T::TN) * 128;
         const uint8_t* sS = st + T::kABytes + T::kBBytes;
@@ -559,7 +488,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     // The step's matrix instructions, sub-tile row by row (route BS: each promote two
     // instructions behind its instruction); hook(t) runs after instruction t.
     v4f p[3];
-    auto mma = [&](const Frags& F, auto&& hook) {
+    auto mma = [&](const Frags& F, auto&& hook) FP8BS_INLINE {
         float srow[T::SI];
         if constexpr (ROUTE == kRouteBS) {
 #pragma unroll
@@ -603,9 +532,9 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
                 asm volatile("" : "+v"(acc[i][j]));
     };
     int cp_tile = 0, cp_kb = 0;  // the step being computed
-    auto finish_step = [&]() {
+    auto finish_step = [&]() FP8BS_INLINE {
         if (++cp_kb == KB) {
-            store_tile(cp_tile, false);
+            store_tile(cp_tile);
             cp_kb = 0;
             ++cp_tile;
         }
@@ -694,6 +623,13 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     float sb_r = 0.f;                            // BS: b_s of the wave's weight block
     int ia[GA];                                  // MX: packed activation scale dwords
     int ib[GB];                                  // MX: packed weight scale dwords
+    // Schedule 2 holds every fragment of a step in registers where they fit beside the
+    // accumulators (64 x 64 per wave: 8 fragments, 64 registers; the 168 registers of a SIMD
+    // running three waves hold them), reading the next step's into each as it falls free.
+    constexpr bool kFullHold = PP == 2 && (T::SI + T::SJ) * 8 + T::SI * T::SJ * 4 <= 128;
+    v8i outer[kFullHold ? NO : 1];  // every fragment of the outer operand (the ring is unused)
+    int ia_n[kFullHold ? GA : 1];   // MX: the next step's scales while the current ones are in use
+    int ib_n[kFullHold ? GB : 1];
 
     auto a_base = [&](const uint8_t* st) { return st + (wm * T::TM) * 128; };
     auto b_base = [&](const uint8_t* st) { return st + T::kABytes + (wn * T::TN) * 128; };
@@ -702,10 +638,10 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
 
     // The head of a step: what its first matrix instruction needs (held fragment 0 and streamed
     // fragment 0), the scales, then the rest of the held fragments.
-    auto read_head = [&](const uint8_t* st) {
+    // The block scales of the step in stage st (route BS: into sa_r / sb_r; MX: into ia / ib, or
+    // into ia_n / ib_n when `next`, while the current ones are still in use).
+    auto read_scales = [&](const uint8_t* st, bool next) FP8BS_INLINE {
         const uint8_t* sS = st + T::kABytes + T::kBBytes;
-        held[0] = frag(held_base(st));
-        ring[0] = frag(streamed(st));
         if constexpr (ROUTE == kRouteBS) {
             const float* sa = (const float*)sS + wm * T::TM + frow;
 #pragma unroll
@@ -713,13 +649,20 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
                 sa_r[i] = sa[16 * i];
             sb_r = ((const float*)(sS + T::kSABytes))[(wn * T::TN) >> 7];
         } else if constexpr (ROUTE == kRouteMX) {
+            int* da = next ? ia_n : ia;
+            int* db = next ? ib_n : ib;
 #pragma unroll
             for (int g = 0; g < GA; ++g)
-                ia[g] = ((const int*)sS)[(wm * T::TM / 64 + g) * 64 + lane];
+                da[g] = ((const int*)sS)[(wm * T::TM / 64 + g) * 64 + lane];
 #pragma unroll
             for (int g = 0; g < GB; ++g)
-                ib[g] = ((const int*)(sS + T::kSABytes))[(wn * T::TN / 64 + g) * 64 + lane];
+                db[g] = ((const int*)(sS + T::kSABytes))[(wn * T::TN / 64 + g) * 64 + lane];
         }
+    };
+    auto read_head = [&](const uint8_t* st) FP8BS_INLINE {
+        held[0] = frag(held_base(st));
+        ring[0] = frag(streamed(st));
+        read_scales(st, false);
 #pragma unroll
         for (int h = 1; h < NH; ++h)
             held[h] = frag(held_base(st) + h * 16 * 128);
@@ -736,7 +679,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     constexpr int kLoadSpacing =
         STAGES >= 3 && NO * NH >= 2 * T::kLoadsPerStep ? (NO * NH) / T::kLoadsPerStep : 1;
     v4f p[3];
-    auto rows = [&](const uint8_t* st, lds_u8* load_st, auto&& transition) {
+    auto rows = [&](const uint8_t* st, lds_u8* load_st, auto&& transition) FP8BS_INLINE {
         const uint8_t* sO = streamed(st);
         float srow[T::SI];
         if constexpr (ROUTE == kRouteBS) {
@@ -754,7 +697,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
         static_for<NO>([&](auto O) {
             constexpr int o = decltype(O)::value;
             if constexpr (o + 1 < NO)
-                ring[(o + 1) & 1] = frag_here(sO + (o + 1) * 16 * 128);
+                ring[(o + 1) & 1] = frag(sO + (o + 1) * 16 * 128);
             static_for<NH>([&](auto H) {
                 constexpr int h = decltype(H)::value;
                 constexpr int t = o * NH + h;
@@ -805,6 +748,89 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
         }
     };
 
+    // ---- schedule 2 with kFullHold: one step with all of its fragments in registers ----------
+    // Every fragment of step s is in registers before its first instruction (read during step
+    // s-1). After the first row of instructions the wave waits for its outstanding reads (the
+    // last ones of step s) and meets the others at the barrier; after it, stage nxt (step s+1)
+    // is complete for everyone and stage st is free for the loaders. The next step's fragments
+    // are then read into the registers as they fall free: outer fragment o after row o, held
+    // fragment h after the last row's instruction h, the last outer fragment after the row.
+    auto read_full = [&](const uint8_t* st) FP8BS_INLINE {
+        read_scales(st, false);
+#pragma unroll
+        for (int o = 0; o < (kFullHold ? NO : 0); ++o)
+            outer[o] = frag(streamed(st) + o * 16 * 128);
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+            held[h] = frag(held_base(st) + h * 16 * 128);
+    };
+    auto rows_full = [&](const uint8_t* nxt, auto&& transition) FP8BS_INLINE {
+        float srow[T::SI];
+        if constexpr (ROUTE == kRouteBS) {
+#pragma unroll
+            for (int i = 0; i < T::SI; ++i)
+                srow[i] = sa_r[i] * sb_r;
+        }
+        auto promote = [&](auto Tc) {
+            constexpr int t = decltype(Tc)::value;
+            constexpr int o = t / NH, h = t % NH;
+            constexpr int i = kStreamA ? o : h;
+            constexpr int j = kStreamA ? h : o;
+            promote_fma(acc[i][j], p[t % 3], srow[i]);
+        };
+        static_for<NO>([&](auto O) {
+            constexpr int o = decltype(O)::value;
+            static_for<NH>([&](auto H) {
+                constexpr int h = decltype(H)::value;
+                constexpr int t = o * NH + h;
+                constexpr int i = kStreamA ? o : h;
+                constexpr int j = kStreamA ? h : o;
+                const v8i& a = kStreamA ? outer[o] : held[h];
+                const v8i& b = kStreamA ? held[h] : outer[o];
+                if constexpr (ROUTE == kRouteBS) {
+                    p[t % 3] = mfma_f8(b, a, v4f{0.f, 0.f, 0.f, 0.f});
+                    if constexpr (t >= 2)
+                        promote(std::integral_constant<int, t - 2>{});
+                } else if constexpr (ROUTE == kRoutePT) {
+                    acc[i][j] = mfma_f8(b, a, acc[i][j]);
+                } else {
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        b, a, acc[i][j], kFmtE4M3, kFmtE4M3, j & 3, ib[j / 4], i & 3, ia[i / 4]);
+                }
+                if constexpr (o == NO - 1)
+                    held[h] = frag(held_base(nxt) + h * 16 * 128);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            if constexpr (o == 0) {
+                transition();
+                __builtin_amdgcn_sched_barrier(0);
+                read_scales(nxt, true);
+            }
+            if constexpr (o < NO - 1)
+                outer[o] = frag(streamed(nxt) + o * 16 * 128);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        outer[NO - 1] = frag(streamed(nxt) + (NO - 1) * 16 * 128);
+#pragma unroll
+        for (int i = 0; i < T::SI; ++i)
+#pragma unroll
+            for (int j = 0; j < T::SJ; ++j)
+                asm volatile("" : "+v"(acc[i][j]));
+        if constexpr (ROUTE == kRouteBS) {
+            asm volatile("" : "+v"(p[0]), "+v"(p[1]), "+v"(p[2]));
+            constexpr int n = T::SI * T::SJ;
+            promote(std::integral_constant<int, n - 2>{});
+            promote(std::integral_constant<int, n - 1>{});
+        } else if constexpr (ROUTE == kRouteMX) {
+#pragma unroll
+            for (int g = 0; g < GA; ++g)
+                ia[g] = ia_n[g];
+#pragma unroll
+            for (int g = 0; g < GB; ++g)
+                ib[g] = ib_n[g];
+        }
+    };
+
     // ---- the step stream ---------------------------------------------------------------------
     // Step s reads stage s % STAGES, and while its matrix instructions run it issues the loads
     // of step s + STAGES - 1 into stage (s - 1) % STAGES. Between the last matrix row of step s
@@ -826,7 +852,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
         constexpr int k = decltype(S)::value;
         return k == 0 ? st0 : k == 1 ? st1 : k == 2 ? st2 : st3;
     };
-    auto step = [&](auto S, int s) {
+    auto step = [&](auto S, int s) FP8BS_INLINE {
         constexpr int kS = decltype(S)::value;
         uint8_t* cur = stage_ptr(S);
         uint8_t* nxt = stage_ptr(std::integral_constant<int, (kS + 1) % STAGES>{});
@@ -841,7 +867,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
             read_head(nxt);
         });
         if (++cp_kb == KB) {
-            store_tile(cp_tile, false);
+            store_tile(cp_tile);
             stores_pending = 1;
             cp_kb = 0;
             ++cp_tile;
@@ -849,13 +875,8 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
     };
     if constexpr (PP >= 2) {
         // Warp-specialised: waves kMathWaves.. only move data, the others only compute. Every
-        // wave passes one barrier before the first step and one per step.
-        // PP == 3: the math waves hold back kHold of a finished tile's stores (all but a
-        // workgroup's last tile) and issue them a few per step after the next steps' barriers,
-        // so that the tiles the CUs finish at the same moment do not meet as one burst of C
-        // writes in the memory path ahead of the loader waves' next loads. The math waves
-        // issue no loads, so their stores are never waited for inside the loop.
-        const int per_step = (T::kHold + KB - 1) / KB;
+        // wave passes one barrier before the first step and one per step. The math waves issue
+        // no loads, so their C stores are never waited for inside the loop.
         if (wave >= T::kMathWaves) {
             if (total > 0) {
                 static_for<STAGES - 1>([&](auto S) {
@@ -867,7 +888,7 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
             }
             // in step s: the loads of step s + STAGES - 1 into the stage step s - 1 used, then
             // wait until those of step s + 1 have landed
-            auto lstep = [&](auto S, int s) {
+            auto lstep = [&](auto S, int s) FP8BS_INLINE {
                 constexpr int kS = decltype(S)::value;
                 plan_loads(s + STAGES - 1 < total);
                 issue_group((lds_u8*)stage_ptr(std::integral_constant<int, (kS + STAGES - 1) % STAGES>{}));
@@ -890,26 +911,34 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
             __builtin_amdgcn_s_waitcnt(0);
             return;
         }
-        auto mstep = [&](auto S, int s) {
+        auto mstep = [&](auto S, int s) FP8BS_INLINE {
             constexpr int kS = decltype(S)::value;
             uint8_t* cur = stage_ptr(S);
             uint8_t* nxt = stage_ptr(std::integral_constant<int, (kS + 1) % STAGES>{});
-            rows(cur, (lds_u8*)nullptr, [&]() {
-                wait_lgkm0();  // this wave's reads of the stage are done
-                __builtin_amdgcn_s_barrier();
-                read_head(nxt);
-            });
-            if constexpr (T::kHold > 0)
-                trickle(per_step);
+            if constexpr (kFullHold) {
+                rows_full(nxt, [&]() {
+                    wait_lgkm0();  // the last reads of this step's stage are done
+                    __builtin_amdgcn_s_barrier();
+                });
+            } else {
+                rows(cur, (lds_u8*)nullptr, [&]() {
+                    wait_lgkm0();  // this wave's reads of the stage are done
+                    __builtin_amdgcn_s_barrier();
+                    read_head(nxt);
+                });
+            }
             if (++cp_kb == KB) {
-                store_tile(cp_tile, T::kHold > 0 && cp_tile + 1 < my_tiles);
+                store_tile(cp_tile);
                 cp_kb = 0;
                 ++cp_tile;
             }
         };
         if (total > 0) {
             __builtin_amdgcn_s_barrier();
-            read_head(st0);
+            if constexpr (kFullHold)
+                read_full(st0);
+            else
+                read_head(st0);
         }
         for (int s = 0; s < total; s += STAGES) {
             mstep(std::integral_constant<int, 0>{}, s);
@@ -924,8 +953,6 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
                     mstep(std::integral_constant<int, 3>{}, s + 3);
             }
         }
-        if constexpr (T::kHold > 0)
-            trickle(T::kHold);  // (nothing is left: the last tile is stored whole)
         __builtin_amdgcn_s_waitcnt(0);
         return;
     }
@@ -1023,10 +1050,7 @@ static hipError_t launch_tile(const GemmArgs& a, const GemmConfig& c, int splits
     X(13, 256, 128, 4, 2, 3, 2)  \
     X(14, 128, 256, 2, 4, 3, 2)  \
     X(15, 256, 128, 2, 2, 3, 2)  \
-    X(16, 128, 128, 2, 2, 3, 2)  \
-    X(17, 256, 128, 4, 2, 3, 3)  \
-    X(18, 128, 256, 2, 4, 3, 3)  \
-    X(19, 128, 128, 2, 2, 3, 3)
+    X(16, 128, 128, 2, 2, 3, 2)
 
 const VariantInfo* variant_info(int v)
 {

@@ -244,10 +244,9 @@ typedef struct {
     int pingpong;    /* schedule. 0: every wave loads and computes; 1: the two halves of an    *
                       * 8-wave workgroup alternate, one running its matrix instructions while  *
                       * the other reads its next operands (2 stages); 2: warp-specialised,     *
-                      * four extra waves issue every global -> LDS load, the others compute;   *
-                      * 3: as 2, and the computing waves hold back part of each finished tile  *
-                      * (all of it with 4 computing waves, half with 8; not a workgroup's last *
-                      * tile) and store it a few pieces per step during the next tile          */
+                      * four extra waves issue every global -> LDS load, the others compute    *
+                      * (with 64 x 64 per computing wave, all of a step's operand fragments    *
+                      * held in registers and the next step's read as registers free up)      */
     int small_m;     /* non-zero: the small-M kernel (every other field is ignored): one        *
                       * workgroup per 16 output columns and 64-row chunk of A streams the      *
                       * weights, its waves split K (M <= 64 * 65535; route MX with the packed  *

@@ -63,7 +63,7 @@ TILES = [(128, 128, 2, 2, 3, 0), (256, 256, 4, 2, 2, 0), (256, 256, 2, 4, 2, 0),
          (256, 128, 2, 2, 3, 0), (128, 256, 2, 4, 3, 0), (256, 128, 4, 2, 3, 0), (128, 64, 2, 1, 3, 0),
          (256, 128, 4, 2, 2, 0), (128, 128, 2, 2, 4, 0), (128, 128, 2, 2, 2, 0), (256, 128, 4, 2, 2, 1),
          (128, 256, 2, 4, 2, 1), (256, 128, 4, 2, 3, 2), (128, 256, 2, 4, 3, 2), (256, 128, 2, 2, 3, 2),
-         (256, 128, 4, 2, 3, 3), (128, 256, 2, 4, 3, 3), (128, 128, 2, 2, 3, 3)]
+         (128, 128, 2, 2, 3, 2)]
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 512, 384), (4160, 3072, 640)])

@@ -179,8 +179,11 @@ fp8bs_config select(int route, int M, int N, int K)
     // 32.5 us, 2304 x 3840 x 4096: 54.0 against 56.9; MX 4352 x 2048 x 7168: 72.9 against 80.3)
     if (tiles(256, 128) > kCUs && 2 * tiles(256, 128) <= 3 * kCUs)
         return square();
+    // of the two, 128 x 256 where it fills the CUs as well: 1-2.5% faster with the same waves
+    // (4096 x 2048 x 7168 52.8 against 53.6 us, 16384 x 1536 x 7168 151.7 against 153.7,
+    // 8192 x 1024 x 4096 32.6 against 33.5, 2048 x 4096 x 7168 52.9 against 53.4)
     if (tiles(256, 128) >= kCUs)
-        return cfg(13, 128);
+        return N % 256 == 0 && tiles(128, 256) >= kCUs ? cfg(14, 256) : cfg(13, 128);
     if (N % 256 == 0 && tiles(128, 256) >= kCUs)
         return cfg(14, 256);
     // 128x128 tiles, unless they would need more rounds of the CUs than the larger ones (7168 x
@@ -194,16 +197,18 @@ fp8bs_config select(int route, int M, int N, int K)
 }
 
 // Split K for route BS: the number of equal K ranges per output tile. With the tiles the
-// selector picks (cfg), a shape whose tiles number fewer than the CUs, at K >= 4096, takes the
+// selector picks (cfg), a shape whose tiles number fewer than the CUs, at K > 4096, takes the
 // most ranges that keep every work unit within one round of the CUs and at least 8 K blocks deep
 // (K/128 must divide evenly); 1 (no split) otherwise. The second pass and its launch cost about
-// 4 us, which shallower K does not repay (measured, 128 x 128 tiles: 1024 x 2048 x 7168, 2
-// ranges: 26.9 us against 30.7; 128 x 7168 x 7168, 4 ranges: 19.2 against 30.3; 512 x 2048 x
-// 4096, 4 ranges: 17.8 against 19.2; 256 x 4096 x 2048, 2 ranges: 15.0 against 11.4).
+// 4 us, which shallower K does not repay (measured, 128 x 128 tiles, plain against split:
+// 256 x 7168 x 7168 25.8 us against 23.2 with 2 ranges; 128 x 7168 x 7168 25.8 against 19.0
+// with 4; 1000 x 1536 x 7168 25.7 against 21.4 with 2; 1024 x 2048 x 7168 25.7 against 25.6
+// with 2; 512 x 2048 x 4096 16.2 against 17.5 with 2 and 17.8 with 4; 256 x 4096 x 2048 10.0
+// against 14.4 with 2).
 int choose_splits(int M, int N, int K, const fp8bs_config& cfg)
 {
     const int kCUs = 256;
-    if (cfg.small_m != 0 || K < 4096)
+    if (cfg.small_m != 0 || K <= 4096)
         return 1;
     const int v = find_variant(cfg);
     if (v < 0 || !fp8bs::split_supported(v))

@@ -89,10 +89,13 @@ def test_select_config_is_shape_driven(fb):
     assert (big.block_m, big.block_n) == (256, 256) and big.xcd_remap == 1
     nn = fb.fp8bs_select_config(fb.ROUTE_BS, 4096, 2048, 7168)
     assert ((4096 + nn.block_m - 1) // nn.block_m) * (2048 // nn.block_n) >= 256
-    # narrow-N: 256x128 tiles, 8 math waves (4x2) plus the four loader waves of schedule 2
-    assert (nn.block_m, nn.block_n, nn.waves_m, nn.waves_n, nn.stages, nn.pingpong) == (256, 128, 4, 2, 3, 2)
+    # narrow-N: 128x256 tiles, 8 math waves (2x4) plus the four loader waves of schedule 2
+    assert (nn.block_m, nn.block_n, nn.waves_m, nn.waves_n, nn.stages, nn.pingpong) == (128, 256, 2, 4, 3, 2)
     nn16 = fb.fp8bs_select_config(fb.ROUTE_BS, 16384, 1536, 7168)
-    assert (nn16.block_m, nn16.block_n, nn16.pingpong) == (256, 128, 2)
+    assert (nn16.block_m, nn16.block_n, nn16.pingpong) == (128, 256, 2)
+    # N not a multiple of 256: 256x128 tiles
+    nn_odd = fb.fp8bs_select_config(fb.ROUTE_BS, 8192, 1920, 7168)
+    assert (nn_odd.block_m, nn_odd.block_n, nn_odd.pingpong) == (256, 128, 2)
     mx = fb.fp8bs_select_config(fb.ROUTE_MX, 4096, 192, 256)  # N % 128 != 0: the 128x64 tile
     assert (mx.small_m, mx.block_n) == (0, 64)
     wide = fb.fp8bs_select_config(fb.ROUTE_BS, 4096, 65536, 1536)  # 1024-tile bands: round-local order
@@ -137,9 +140,10 @@ def test_select_config_is_shape_driven(fb):
     c = fb.fp8bs_select_config(fb.ROUTE_BS, 64, 40960 - 128, 1536)  # 319 tiles: two rounds
     assert (c.block_m, c.block_n, c.pingpong) == (128, 128, 2)
     # 256x128 tiles just past one round (257 to 384): 128x128 ones instead; at 256 and from 385
-    # 256x128
+    # the larger tiles, 128x256 where N % 256 == 0
     for route, shape, tile in ((fb.ROUTE_BS, (1280, 7168, 2048), (128, 128)), (fb.ROUTE_MX, (4352, 2048, 7168), (128, 128)),
-                               (fb.ROUTE_BS, (4096, 2048, 7168), (256, 128)), (fb.ROUTE_BS, (1664, 7168, 2048), (256, 128))):
+                               (fb.ROUTE_BS, (4096, 2048, 7168), (128, 256)), (fb.ROUTE_BS, (1664, 7168, 2048), (128, 256)),
+                               (fb.ROUTE_BS, (4096, 1920, 7168), (256, 128))):
         c = fb.fp8bs_select_config(route, *shape)
         assert (c.block_m, c.block_n, c.pingpong) == (*tile, 2), (route, shape)
     c = fb.fp8bs_select_config(fb.ROUTE_BS, 129, 65536, 1536)
@@ -148,8 +152,9 @@ def test_select_config_is_shape_driven(fb):
     c = fb.fp8bs_select_config(fb.ROUTE_BS, 64, 36864, 7168)
     assert (c.block_m, c.block_n, c.pingpong) == (128, 256, 2)
     # 256x256 tiles from one round of the CUs for route MX, from two for the others
-    assert (fb.fp8bs_select_config(fb.ROUTE_MX, 256, 65536, 1536).block_m,
-            fb.fp8bs_select_config(fb.ROUTE_BS, 1024, 24576, 1536).block_n) == (256, 128)
+    assert fb.fp8bs_select_config(fb.ROUTE_MX, 256, 65536, 1536).block_m == 256
+    c = fb.fp8bs_select_config(fb.ROUTE_BS, 1024, 24576, 1536)
+    assert (c.block_m, c.block_n) == (128, 256)
     # 128x128 tiles only while they need no more rounds of the CUs than 256x128 tiles
     for shape, tile in (((640, 7168, 7168), (256, 128)), ((1024, 7168, 7168), (256, 128)),
                         ((1024, 3072, 7168), (128, 128)), ((1024, 2048, 7168), (128, 128)),
@@ -297,6 +302,7 @@ def test_splitk_sizes_and_host_rejections(fb):
     assert fb.fp8bs_splitk_workspace_bytes(100, 100, 128, 0) == 0     # a shape route BS rejects
     assert fb.fp8bs_splitk_workspace_bytes(256, 4096, 2048, 0) == 0   # too shallow to repay the second pass
     assert fb.fp8bs_splitk_workspace_bytes(128, 7168, 7168, 0) == 4 * 128 * 7168 * 4
+    assert fb.fp8bs_splitk_workspace_bytes(512, 2048, 4096, 0) == 0   # K = 4096: splitting does not pay
     p = 0x10000
     L = fb.lib
     assert L.fp8bs_gemm_splitk(p, p, p, p, p, 1024, 2048, 7168, 0, None, 0, None) == 6

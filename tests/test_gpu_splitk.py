@@ -23,7 +23,7 @@ def _operands(fb, x):
     return to_dev(x.A), to_dev(x.a_scale_kmajor), fb.prep_weights(to_dev(x.B)), to_dev(x.b_scale)
 
 
-@pytest.mark.parametrize("M,N,K", [(1024, 2048, 7168), (600, 2048, 4096), (128, 7168, 7168), (1000, 1536, 7168)])
+@pytest.mark.parametrize("M,N,K", [(1024, 2048, 7168), (600, 2048, 5120), (128, 7168, 7168), (1000, 1536, 7168)])
 def test_splitk_library_choice(fb, oracle, M, N, K):
     x = workload.bs_inputs(M, N, K, 11)
     A, sa, Bp, sb = _operands(fb, x)

@@ -29,7 +29,7 @@ def _noalloc(fb, A, sa, Bp, sb, C, M, N, K, splits):
 def test_noalloc_matches_workspace_entry(fb, oracle, order):
     # first call 16 MiB of partial tiles (2 ranges), the second a smaller input (600 rows,
     # 2 ranges, 9.4 MiB): the second reads only what it wrote itself
-    for i, (M, N, K) in enumerate([(1024, 2048, 7168), (600, 2048, 4096)]):
+    for i, (M, N, K) in enumerate([(1024, 2048, 7168), (600, 2048, 5120)]):
         x = workload.bs_inputs(M, N, K, 21 + i)
         A, sa, Bp, sb = to_dev(x.A), to_dev(x.a_scale_kmajor), fb.prep_weights(to_dev(x.B)), to_dev(x.b_scale)
         assert 0 < fb.fp8bs_splitk_workspace_bytes(M, N, K, 0) <= fb.SPLITK_SCRATCH_BYTES

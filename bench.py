@@ -38,6 +38,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--preroll-ms P] [--n
                                                           least-squares fit fixed + slope * K/128)
        python bench.py --tile-sweep NAME                (every tile order (group_m, XCD mapping)
                                                           and instantiated tile on one workload)
+       python bench.py --loop-probe NAME                (the loop skeleton's parts one at a time
+                                                          on the workload's operand bytes)
 """
 from __future__ import annotations
 
@@ -273,6 +275,54 @@ def mfma_ceiling(case: Case, stream, iters: int = 512) -> dict:
     tflops = flops / (e0.elapsed_time(e1) / 1e3) / 1e12
     return {"tflops": round(tflops, 1), "frac_of_peak": round(tflops / PEAK_FP8_TFLOPS, 4),
             "operands": f"{case.name} A and prepared B fragments", "kernel": "mfma_ceiling_kernel"}
+
+
+# the loop skeleton's part masks, in the order the parts are added (fp8bs_loop_probe)
+LOOP_PROBE_ROWS = [(0, "64x64 per wave: matrix instructions only (operands in registers)"),
+                   (1, "+ fragment reads from LDS"),
+                   (3, "+ four loader waves (48 KB per step global -> LDS) and a barrier per step"),
+                   (7, "+ the BS promote"),
+                   (15, "+ the C stores of a 256x128 tile every 6 steps"),
+                   (5, "64x64: the BS promote alone (no LDS, no loads)"),
+                   (17, "128x64 per wave: fragment reads from LDS"),
+                   (19, "+ the computing waves' own loads (64 KB per step) and a barrier per step"),
+                   (23, "+ the BS promote"),
+                   (31, "+ the C stores of a 256x256 tile every 6 steps")]
+
+
+def loop_probe_mode(name: str, stream, steps: int = 600) -> int:
+    """fp8bs_loop_probe for every row of LOOP_PROBE_ROWS on the workload's operand bytes:
+    the minimum over 3 runs of 5 back-to-back launches (HIP events on the stream), after a
+    pre-roll, as matrix TFLOP/s and the fraction of the dense peak."""
+    import torch
+
+    import fp8_block_scaled_e4m3_amd as fb
+    case = Case(name, 0, stream)
+    sink = torch.empty(256 * 8 * 4, dtype=torch.float32, device=case.A.device)
+    rows = []
+    for parts, what in LOOP_PROBE_ROWS:
+        nout = fb.lib.fp8bs_loop_probe_out_bytes(parts)
+        out = torch.empty(max(nout * 8, 16), dtype=torch.uint8, device=case.A.device)  # 8 slots of tiles
+        launch = lambda: fb.fp8bs_loop_probe(parts, case.A, case.B, case.N, steps, sink, out, stream)
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.1:
+            launch()
+            torch.cuda.synchronize()
+        best = None
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            flops = sum(launch() for _ in range(5))
+            e1.record(stream)
+            torch.cuda.synchronize()
+            rate = flops / (e0.elapsed_time(e1) / 1e3) / 1e12
+            best = rate if best is None else max(best, rate)
+        rows.append(dict(parts=parts, what=what, tflops=round(best, 1), frac=round(best / PEAK_FP8_TFLOPS, 4)))
+        log(f"[bench] loop probe {parts}: {rows[-1]}")
+        del out
+    print(json.dumps({"mode": "loop_probe", "workload": name, "steps": steps, "rows": rows}), flush=True)
+    return 0
 
 
 def sampled_parity(case: Case, nrows: int = 16, ncols: int = 16) -> dict:
@@ -780,7 +830,7 @@ def profile_md(name: str, trace_dir: str, pmc_dirs: list[str], timed: int) -> in
 
 
 def sweep_md(path: str) -> int:
-    """Markdown of a --ksweep or --tile-sweep JSON line (the file holds bench.py's stdout)."""
+    """Markdown of a --ksweep, --tile-sweep or --loop-probe JSON line (the file holds bench.py's stdout)."""
     with open(path) as f:
         d = json.loads(f.read().strip().splitlines()[-1])
     out = []
@@ -804,6 +854,17 @@ def sweep_md(path: str) -> int:
             out.append(f"| {r} | {v['fixed_us']} | {v['us_per_k_block']} | {v['max_residual_us']} |")
         cfg = d["routes"]["bs"]["points"][0]["config"]
         out += ["", f"Configuration (both routes): {cfg}."]
+    elif d["mode"] == "loop_probe":
+        out += [f"# Loop skeleton on the {d['workload']} operand bytes", "",
+                "Command (R = repository root):", "", "```",
+                f"python3 R/bench.py --loop-probe {d['workload']} > OUT/loop_probe.json",
+                "python3 R/bench.py --sweep-md OUT/loop_probe.json", "```", "",
+                "fp8bs_loop_probe (csrc/probe.hip): one workgroup per CU, eight computing waves (two per SIMD),",
+                f"{d['steps']} steps per launch; the GEMM mainloop's parts added one at a time. Rate: matrix",
+                "instructions only, best of 3 runs of 5 back-to-back launches (HIP events), after a 0.1 s pre-roll.", "",
+                "| parts mask | loop | TFLOP/s | of the 5.0 PFLOP/s peak |", "|---|---|---|---|"]
+        for r in d["rows"]:
+            out.append(f"| {r['parts']} | {r['what']} | {r['tflops']} | {r['frac']} |")
     else:
         rows = d["rows"]
         sel = rows[0]
@@ -842,10 +903,11 @@ def main() -> int:
     ap.add_argument("--ksweep-k", default="1024,2048,3584,7168")
     ap.add_argument("--tile-sweep", default=None)
     ap.add_argument("--splitk", action="store_true", help="only the split-K rows")
+    ap.add_argument("--loop-probe", default=None, help="NAME: the loop skeleton on a workload's operands")
     ap.add_argument("--summarize-pmc", nargs="+", default=None,
                     help="rocprofv3 --pmc output dirs -> median counters and utilisations (JSON)")
     ap.add_argument("--pmc-pass", default=None, help="print the counters of pass a or b (for --pmc)")
-    ap.add_argument("--sweep-md", default=None, help="FILE: markdown of a --ksweep / --tile-sweep output")
+    ap.add_argument("--sweep-md", default=None, help="FILE: markdown of a --ksweep / --tile-sweep / --loop-probe output")
     ap.add_argument("--profile-md", nargs="+", default=None,
                     help="NAME TRACE_DIR [PMC_DIR ...] -> markdown summary of the rocprofv3 runs")
     args = ap.parse_args()
@@ -882,6 +944,9 @@ def main() -> int:
     if args.tile_sweep:
         with torch.cuda.stream(stream):
             return tile_sweep_mode(args.tile_sweep, stream)
+    if args.loop_probe:
+        with torch.cuda.stream(stream):
+            return loop_probe_mode(args.loop_probe, stream)
     if args.splitk:
         with torch.cuda.stream(stream):
             print(json.dumps({"mode": "splitk", "rows": splitk_rows(stream)}), flush=True)

@@ -27,7 +27,7 @@ __all__ = [
     "fp8mx_packed_scale_bytes", "fp8mx_scale_bytes", "fp8mx_pack_a_scale", "fp8mx_prep_weights", "fp8mx_gemm",
     "prep_weights", "mx_prep_weights", "mx_pack_a_scale",
     "Config", "ROUTE_BS", "ROUTE_MX", "fp8bs_select_config", "fp8bs_gemm_with_config", "fp8mx_gemm_with_config",
-    "fp8bs_mfma_ceiling", "ROUTE_PT", "fp8pt_gemm", "fp8pt_gemm_with_config",
+    "fp8bs_mfma_ceiling", "fp8bs_loop_probe", "ROUTE_PT", "fp8pt_gemm", "fp8pt_gemm_with_config",
     "IN_F32", "IN_BF16", "fp8bs_quantize_act", "fp8mx_quantize_act", "quantize_bs", "quantize_mx",
     "fp8mx_gemm_small_m", "fp8bs_splitk_workspace_bytes", "fp8bs_gemm_splitk", "splitk_workspace",
     "fp8bs_gemm_splitk_noalloc", "SPLITK_SCRATCH_BYTES",
@@ -54,6 +54,8 @@ SIGNATURES = {
     "fp8bs_gemm_with_config": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp, _vp]),
     "fp8mx_gemm_with_config": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp, _vp]),
     "fp8bs_mfma_ceiling": (_int, [_vp, _vp, _int, _int, _int, _int, _vp, _int, _vp, _vp]),
+    "fp8bs_loop_probe_out_bytes": (ctypes.c_size_t, [_int]),
+    "fp8bs_loop_probe": (_int, [_int, _vp, _vp, _int, _int, _int, _int, _vp, ctypes.c_size_t, _vp, _int, _vp, _vp]),
     "fp8pt_gemm": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp]),
     "fp8bs_quantize_act": (_int, [_vp, _int, _vp, _vp, _int, _int, _vp]),
     "fp8mx_gemm_small_m": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _vp]),
@@ -382,6 +384,28 @@ def fp8bs_mfma_ceiling(A: torch.Tensor, B_prep: torch.Tensor, N: int, iters: int
     flops = ctypes.c_longlong(0)
     _check("fp8bs_mfma_ceiling", lib.fp8bs_mfma_ceiling(_ptr(A), _ptr(B_prep), M, N, K, iters, _ptr(sink),
                                                         sink.numel(), ctypes.byref(flops), _stream(stream)))
+    return flops.value
+
+
+LP_READS, LP_LOADS, LP_PROMOTE, LP_STORES, LP_BIG = 1, 2, 4, 8, 16
+
+
+def fp8bs_loop_probe(parts: int, A: torch.Tensor, B_prep: torch.Tensor, N: int, steps: int, sink: torch.Tensor,
+                     out: torch.Tensor | None = None, stream=None) -> int:
+    """Launch the loop-skeleton probe (parts: a mask of the LP_* parts) on A [M,K] and prepared
+    weights of N rows; returns the launch's matrix FLOP count (time it with events)."""
+    fn = "fp8bs_loop_probe"
+    M, K = _matrix(fn, "A", A, _CODE_DTYPES)
+    _expect(fn, "B_prep", B_prep, _CODE_DTYPES)
+    _expect(fn, "sink", sink, (torch.float32,))
+    if out is not None:
+        _same_device(fn, A, B_prep, sink, out)
+    else:
+        _same_device(fn, A, B_prep, sink)
+    flops = ctypes.c_longlong(0)
+    _check(fn, lib.fp8bs_loop_probe(parts, _ptr(A), _ptr(B_prep), M, N, K, steps,
+                                    _ptr(out) if out is not None else None, out.numel() * out.element_size() if out is not None else 0,
+                                    _ptr(sink), sink.numel(), ctypes.byref(flops), _stream(stream)))
     return flops.value
 
 

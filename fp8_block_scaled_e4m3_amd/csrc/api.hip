@@ -583,4 +583,29 @@ int fp8bs_mfma_ceiling(const void* A, const void* B_prep, int M, int N, int K, i
     return hip_status(fp8bs::launch_mfma_ceiling(A, B_prep, M, N, K, iters, sink, sink_len, flops, stream));
 }
 
+size_t fp8bs_loop_probe_out_bytes(int parts)
+{
+    return fp8bs::loop_probe_parts_ok(parts) ? fp8bs::loop_probe_out_bytes(parts) : 0;
+}
+
+int fp8bs_loop_probe(int parts, const void* A, const void* B_prep, int M, int N, int K, int steps, void* out,
+                     size_t out_bytes, float* sink, int sink_len, long long* flops, hipStream_t stream)
+{
+    if (!fp8bs::loop_probe_parts_ok(parts))
+        return FP8BS_E_CONFIG;
+    const size_t step_bytes = (parts & 16) ? 64 * 1024 : 48 * 1024;
+    if (M < 1 || N < 1 || K < 128 || K % 128 != 0 || steps < 1 || !fits_offsets(M, N, K) ||
+        (size_t)M * K < std::max<size_t>(step_bytes, 32 * 1024) || (size_t)N * K < 32 * 1024)
+        return FP8BS_E_SHAPE;
+    const size_t need = fp8bs::loop_probe_out_bytes(parts);
+    if (!A || !B_prep || !sink || (need && !out))
+        return FP8BS_E_NULL;
+    if (!aligned(A, 16) || !aligned(B_prep, 16) || !aligned(sink, 4) || (need && !aligned(out, 16)))
+        return FP8BS_E_ALIGN;
+    if (need > out_bytes || sink_len < 8 * 256)
+        return FP8BS_E_WORKSPACE;
+    return hip_status(fp8bs::launch_loop_probe(parts, A, B_prep, (size_t)M * K, steps, out, out_bytes, sink, sink_len,
+                                               flops, stream));
+}
+
 }  // extern "C"

@@ -70,6 +70,12 @@ constexpr size_t kSplitkScratchBytes = (size_t)32 << 20;
 void* splitk_scratch();
 hipError_t launch_mfma_ceiling(const void* A, const void* B_prep, int M, int N, int K, int iters, float* sink,
                                int sink_len, long long* flops, hipStream_t stream);
+// Loop skeleton probe (probe.hip): `parts` a mask of the kLp* parts, one of the instantiated
+// combinations; out: bytes for the stored tiles (parts with kLpStores), rotated over whole slots.
+bool loop_probe_parts_ok(int parts);
+size_t loop_probe_out_bytes(int parts);
+hipError_t launch_loop_probe(int parts, const void* A, const void* B_prep, size_t a_bytes, int steps, void* out,
+                             size_t out_bytes, float* sink, int sink_len, long long* flops, hipStream_t stream);
 hipError_t launch_prep_weights(const void* B, void* B_prep, int N, int K, hipStream_t stream);
 hipError_t launch_pack_scales(const void* e8m0, void* packed, int rows, int K, int permute, hipStream_t stream);
 // Small-M kernel (decode.hip): M >= 1 in chunks of kDecodeMaxRows rows (at most kDecodeMaxChunks

@@ -289,6 +289,35 @@ int fp8pt_gemm_with_config(const void *A, const float *a_scale, const void *B_pr
 int fp8bs_mfma_ceiling(const void *A, const void *B_prep, int M, int N, int K, int iters, float *sink,
                        int sink_len, long long *flops, hipStream_t stream);
 
+/* Diagnostic (not part of the GEMM): a skeleton of the GEMM mainloop with its parts switched on
+ * one at a time, to measure what each costs the matrix core (page "Flydsl Fp8 Blockscale Gemm",
+ * Bottleneck diagnosis: identical matrix work, phases added one by one). One workgroup per CU,
+ * eight computing waves, `steps` steps of (TM/16) x 4 instructions of 16x16x128 per wave on
+ * operand bytes taken from A [M,K] and B_prep. parts, a mask:
+ *   1 (FP8BS_LP_READS)   every step reads the wave's operand fragments from LDS (the GEMM's
+ *                        swizzled 16-byte reads), else the operands stay in registers;
+ *   2 (FP8BS_LP_LOADS)   48 KB per step (64 KB with FP8BS_LP_BIG) of A's bytes go global -> LDS
+ *                        (buffer_load ... lds) by four extra loader waves (by the computing waves
+ *                        with FP8BS_LP_BIG), with one workgroup barrier per step;
+ *   4 (FP8BS_LP_PROMOTE) route BS's promote after each instruction;
+ *   8 (FP8BS_LP_STORES)  every 6 steps each computing wave stores its TM x 64 block (2 bytes an
+ *                        element) to `out`;
+ *  16 (FP8BS_LP_BIG)     TM = 128 instead of 64.
+ * Instantiated masks: 0, 1, 3, 5, 7, 15, 17, 19, 23, 31; others return FP8BS_E_CONFIG. The
+ * results are meaningless; only the launch time is (time it with events on `stream`).
+ * Needs M*K >= 64 KB and N*K >= 32 KB; out: fp8bs_loop_probe_out_bytes(parts) bytes or more
+ * (rotated over whole slots of that size), 16-byte aligned, NULL allowed when that is 0;
+ * sink: >= 8 floats per CU; flops (may be NULL) receives the launch's matrix FLOP count.
+ * FP8BS_E_WORKSPACE if out or sink is short. */
+#define FP8BS_LP_READS 1
+#define FP8BS_LP_LOADS 2
+#define FP8BS_LP_PROMOTE 4
+#define FP8BS_LP_STORES 8
+#define FP8BS_LP_BIG 16
+size_t fp8bs_loop_probe_out_bytes(int parts);
+int fp8bs_loop_probe(int parts, const void *A, const void *B_prep, int M, int N, int K, int steps, void *out,
+                     size_t out_bytes, float *sink, int sink_len, long long *flops, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

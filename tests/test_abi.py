@@ -314,3 +314,19 @@ def test_splitk_sizes_and_host_rejections(fb):
     assert L.fp8bs_gemm_splitk(None, p, p, p, p, 1024, 2048, 7168, 2, p, 1 << 30, None) == 1
     assert L.fp8bs_gemm_splitk(p, p, p, p, p, 0, 2048, 7168, 2, None, 0, None) == 0
     assert fb.fp8bs_strerror(6).startswith("the workspace")
+
+
+def test_loop_probe_host_rejections(fb):
+    """The loop-skeleton probe's host checks: unknown part masks, small operands, NULL or short
+    buffers are rejected before anything is launched."""
+    L, p = fb.lib, 0x1000
+    assert L.fp8bs_loop_probe_out_bytes(2) == 0          # not an instantiated mask
+    assert L.fp8bs_loop_probe_out_bytes(7) == 0          # no stores, no output
+    assert L.fp8bs_loop_probe_out_bytes(15) > 0 and L.fp8bs_loop_probe_out_bytes(31) == 2 * L.fp8bs_loop_probe_out_bytes(15)
+    assert L.fp8bs_loop_probe(2, p, p, 512, 512, 1024, 10, None, 0, p, 4096, None, None) == 4
+    assert L.fp8bs_loop_probe(1, p, p, 64, 64, 128, 10, None, 0, p, 4096, None, None) == 2
+    assert L.fp8bs_loop_probe(1, None, p, 512, 512, 1024, 10, None, 0, p, 4096, None, None) == 1
+    assert L.fp8bs_loop_probe(15, p, p, 512, 512, 1024, 10, None, 0, p, 4096, None, None) == 1
+    assert L.fp8bs_loop_probe(15, p, p, 512, 512, 1024, 10, p, 100, p, 4096, None, None) == 6
+    assert L.fp8bs_loop_probe(1, p, p, 512, 512, 1024, 10, None, 0, p, 100, None, None) == 6
+    assert L.fp8bs_loop_probe(1, p + 4, p, 512, 512, 1024, 10, None, 0, p, 4096, None, None) == 3

@@ -2,8 +2,9 @@
 // a skeleton of the GEMM mainloop that adds its ingredients one at a time.
 //
 // The gfx950 matrix core slows down when the operand bits change from one instruction to the
-// next (measured: ~97% of the nominal rate on constant operands, ~45% on random or quantised
-// operand bytes). This kernel measures that data-dependent ceiling directly: every wave loads
+// next (measured: ~97% of the nominal rate on constant operands, ~75% in this kernel on the
+// narrow-N workload's quantised bytes). This kernel measures that data-dependent ceiling
+// directly: every wave loads
 // four activation and four weight fragments from A and the prepared B (the same per-lane
 // layout the GEMM uses), then runs back-to-back v_mfma_f32_16x16x128_f8f6f4 on them with no
 // memory traffic, in the GEMM's issue order (one operand changes per instruction). It is the

@@ -75,7 +75,7 @@ class Config(ctypes.Structure):
     """fp8bs_config of include/fp8bs.h."""
     _fields_ = [(n, ctypes.c_int) for n in
                 ("block_m", "block_n", "waves_m", "waves_n", "stages", "group_m", "xcd_remap", "persistent",
-                 "pingpong", "small_m")]
+                 "pingpong", "small_m", "c_store")]
 
     def as_dict(self) -> dict:
         return {n: getattr(self, n) for n, _ in self._fields_}

@@ -60,7 +60,7 @@ int find_variant(const fp8bs_config& c)
     }
 }
 
-fp8bs_config make_config(int variant, int group_m, int xcd_remap, int persistent)
+fp8bs_config make_config(int variant, int group_m, int xcd_remap, int persistent, int c_store)
 {
     const fp8bs::VariantInfo* vi = fp8bs::variant_info(variant);
     fp8bs_config c;
@@ -74,6 +74,7 @@ fp8bs_config make_config(int variant, int group_m, int xcd_remap, int persistent
     c.xcd_remap = xcd_remap;
     c.persistent = persistent;
     c.small_m = 0;
+    c.c_store = c_store;
     return c;
 }
 
@@ -109,9 +110,27 @@ fp8bs_config select(int route, int M, int N, int K)
     // weight panel is reused by the tile rows that need it while it is still cached (measured
     // on the 4096 x 65536 x 1536 shape: about 12% faster than mapping 1, 5% faster than
     // round-robin; on the 16384 x 8192 x 1280 shape mapping 1 is 6% faster than mapping 2).
+    // C store policy (all three give the same bits; measured per shape, each policy forced
+    // through the *_with_config entry, alternating, on three boxes):
+    //  * C larger than the 256 MiB memory-side cache: written through as non-temporal lines
+    //    (2), which keeps C from pushing the operands out of that cache (4096 x 65536 x 1536:
+    //    392.8 against 403.3 us; written through without the hint, 423 against 413).
+    //  * At most three rounds of tiles: written through the L2 (1). A few rounds' stores come
+    //    close to the kernel's end, and lines still dirty in the L2s then are written back
+    //    after the last tile (4096 x 2048 x 7168: 51.0 against 52.5 us, the route-PT twin 43.8
+    //    against 45.5; 4096 x 8192 x 1536, two rounds: 50.2 against 51.9; 16384 x 1536 x 7168,
+    //    three rounds: 148.5 against 149.4).
+    //  * Otherwise the ordinary write-back stores: with more rounds the L2 absorbs each round's
+    //    burst (16384 x 5120 x 2048, five rounds: 137.6 against 138.5 written through, 140.5
+    //    non-temporal; 16384 x 7168 x 768, seven rounds: from 3% faster to 5% slower written
+    //    through depending on the box, 4-7% slower non-temporal).
     auto cfg = [&](int variant, int block_n) {
         const int xcd = group_m * (N / block_n) <= 2 * kCUs ? 1 : 2;
-        return make_config(variant, group_m, xcd, 1);
+        const int block_m = fp8bs::variant_info(variant)->block_m;
+        const int c_store = (int64_t)M * N * 2 > ((int64_t)256 << 20) ? 2
+                            : tiles(block_m, block_n) <= 3 * kCUs     ? 1
+                                                                      : 0;
+        return make_config(variant, group_m, xcd, 1, c_store);
     };
     // The small-M kernel against the main kernel. With few rows the main kernel runs one round
     // of 128-row tiles whose time is set by the K loop (warp-specialised 128 x 128 tiles, route
@@ -235,12 +254,14 @@ int check_config(int route, const fp8bs_config* c, int N, fp8bs::GemmConfig* out
         return FP8BS_E_CONFIG;  // handled by run()
     const int v = find_variant(*c);
     if (v < 0 || !fp8bs::variant_supports(route, v) || c->group_m < 1 || N % c->block_n != 0 ||
-        (c->xcd_remap < 0 || c->xcd_remap > 2) || (c->persistent != 0 && c->persistent != 1))
+        (c->xcd_remap < 0 || c->xcd_remap > 2) || (c->persistent != 0 && c->persistent != 1) ||
+        (c->c_store < 0 || c->c_store > 2))
         return FP8BS_E_CONFIG;
     out->variant = v;
     out->group_m = c->group_m;
     out->xcd_remap = c->xcd_remap;
     out->persistent = c->persistent;
+    out->c_store = c->c_store;
     return FP8BS_OK;
 }
 

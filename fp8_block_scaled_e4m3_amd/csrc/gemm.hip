@@ -131,6 +131,11 @@ __device__ __forceinline__ void wait_lgkm0()
     __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14));
 }
 
+// Cache-policy bits of a vector memory store: sc1 alone is device scope (written through the
+// XCD's L2, which other XCDs do not see), nt marks the line non-temporal (streamed, not kept).
+constexpr int kCpolThrough = 16;             // sc1
+constexpr int kCpolStreamThrough = 16 | 2;   // sc1 nt
+
 // Buffer resource for a byte buffer starting at `base` (range check at 2^31 - 1 bytes).
 __device__ __forceinline__ v4i buffer_desc(const void* base)
 {
@@ -212,7 +217,7 @@ __global__ void __launch_bounds__((WM * WN + (PP >= 2 ? 4 : 0)) * 64)
 gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
             const uint8_t* __restrict__ B, const void* __restrict__ b_scale,
             uint16_t* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n,
-            int group_m, int xcd_remap, int ksplit, float* __restrict__ partial)
+            int group_m, int xcd_remap, int ksplit, float* __restrict__ partial, int c_store)
 {
     using T = Tile<ROUTE, BM, BN, WM, WN, STAGES, PP>;
     // One LDS array per stage: the stage of every read is known at compile time, so the
@@ -413,8 +418,13 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
 #pragma unroll
         for (int si = 0; si < T::SI; ++si) {
             const int m = mbase + 16 * si;
+            // the 16 rows of this sub-tile row through one buffer resource based at its first
+            // row: byte offsets stay below 16 rows * 2N bytes <= 2^29 (N * K < 2^31, K >= 128)
+            const int mblk = tm * BM + wm * T::TM + 16 * si;
+            const __amdgpu_buffer_rsrc_t crs =
+                __builtin_amdgcn_make_buffer_rsrc(C + (size_t)mblk * N, 0, 0x7fffffff, 0x00020000);
+            const int cbyte = (frow * N + nbase) * 2;
             if (m < M) {
-                uint16_t* crow = C + (size_t)m * N + nbase;
 #pragma unroll
                 for (int sj = 0; sj < T::SJ; sj += 2) {
                     v4f lo = acc[si][sj];
@@ -428,7 +438,14 @@ gemm_kernel(const uint8_t* __restrict__ A, const void* __restrict__ a_scale,
                     packed.y = (int)pack_bf16x2(lo.z, lo.w);
                     packed.z = (int)pack_bf16x2(hi.x, hi.y);
                     packed.w = (int)pack_bf16x2(hi.z, hi.w);
-                    *(v4i*)(crow + 32 * (sj >> 1)) = packed;
+                    // the policy is an immediate of the instruction; c_store is uniform
+                    const int off = cbyte + 64 * (sj >> 1);
+                    if (c_store == 2)
+                        __builtin_amdgcn_raw_buffer_store_b128(packed, crs, off, 0, kCpolStreamThrough);
+                    else if (c_store == 1)
+                        __builtin_amdgcn_raw_buffer_store_b128(packed, crs, off, 0, kCpolThrough);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b128(packed, crs, off, 0, 0);
                 }
             }
 #pragma unroll
@@ -1029,7 +1046,7 @@ static hipError_t launch_tile(const GemmArgs& a, const GemmConfig& c, int splits
         grid = units;
     return launch_kernel(kernel, dim3(grid), dim3(T::kThreads), a.stream, (const uint8_t*)a.A, a.a_scale,
                          (const uint8_t*)a.B, a.b_scale, (uint16_t*)a.C, a.M, a.N, a.K, tiles_m, tiles_n,
-                         c.group_m > 0 ? c.group_m : 1, c.xcd_remap, SPLIT ? splits : 1, partial);
+                         c.group_m > 0 ? c.group_m : 1, c.xcd_remap, SPLIT ? splits : 1, partial, c.c_store);
 }
 
 // Instantiated shapes: {BM, BN, WM, WN, STAGES, ping-pong}. Index = GemmConfig::variant.

@@ -52,6 +52,7 @@ struct GemmConfig {
     int group_m;     // tile rows walked together by consecutive tiles
     int xcd_remap;   // give each XCD a contiguous range of the tile order
     int persistent;  // 1: one workgroup per CU slot looping over tiles; 0: one per tile
+    int c_store;     // C store cache policy: 0 write-back, 1 write-through, 2 write-through non-temporal
 };
 
 const VariantInfo* variant_info(int v);

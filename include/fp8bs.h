@@ -257,6 +257,12 @@ typedef struct {
                       * weight sub-tiles per workgroup (at most 32 rows per launch chunk, N %  *
                       * 32 == 0). Same results for all up to 48 rows; other values, or 4 where *
                       * it does not apply, are rejected with FP8BS_E_CONFIG                    */
+    int c_store;     /* cache policy of the main kernel's C stores (the small-M kernel and the  *
+                      * split-K partial sums ignore it). 0: ordinary stores, kept in the       *
+                      * XCD's write-back L2 until evicted; 1: written through the L2 at device *
+                      * scope; 2: written through and marked non-temporal, so C streams past  *
+                      * the caches instead of displacing the operands held there. Same bits   *
+                      * for all three; any other value is rejected with FP8BS_E_CONFIG        */
 } fp8bs_config;
 
 /* The configuration fp8bs_gemm (route FP8BS_ROUTE_BS), fp8mx_gemm (FP8BS_ROUTE_MX) or

@@ -100,6 +100,14 @@ def test_select_config_is_shape_driven(fb):
     assert (mx.small_m, mx.block_n) == (0, 64)
     wide = fb.fp8bs_select_config(fb.ROUTE_BS, 4096, 65536, 1536)  # 1024-tile bands: round-local order
     assert (wide.block_m, wide.block_n) == (256, 256) and wide.xcd_remap == 2
+    # C stores: non-temporal and written through for a C larger than 256 MiB, written through
+    # for at most three rounds of tiles, ordinary stores otherwise
+    assert nn.c_store == 1 and wide.c_store == 2 and big.c_store == 0 and nn16.c_store == 1
+    for route, shape, policy in ((fb.ROUTE_MX, (16384, 8192, 1280), 0), (fb.ROUTE_MX, (16384, 8192 + 256, 1280), 2),
+                                 (fb.ROUTE_BS, (4096, 8192, 1536), 1), (fb.ROUTE_PT, (4096, 2048, 7168), 1),
+                                 (fb.ROUTE_BS, (128, 65536, 1536), 1), (fb.ROUTE_BS, (1, 128, 128), 0),
+                                 (fb.ROUTE_MX, (16384, 5120, 2048), 0)):
+        assert fb.fp8bs_select_config(route, *shape).c_store == policy, (route, shape)
     for route, shape in ((fb.ROUTE_BS, (4096, 65536, 1536)), (fb.ROUTE_MX, (16384, 8192, 1280)),
                          (fb.ROUTE_BS, (128, 256, 512)), (fb.ROUTE_BS, (1, 128, 128))):
         c = fb.fp8bs_select_config(route, *shape)
@@ -189,6 +197,16 @@ def test_small_m_limits_rejected_on_the_host(fb):
     bad = fb.Config()
     bad.small_m = 5
     assert fb.lib.fp8bs_gemm_with_config(p, p, p, p, p, 8, 256, 256, ctypes.byref(bad), None) == 4
+
+
+def test_store_policy_out_of_range_rejected(fb):
+    """c_store other than 0, 1 or 2 is a configuration error, found before any launch."""
+    p = 0x10000
+    for policy in (-1, 3):
+        for fn in (fb.lib.fp8bs_gemm_with_config, fb.lib.fp8pt_gemm_with_config, fb.lib.fp8mx_gemm_with_config):
+            cfg = fb.fp8bs_select_config(fb.ROUTE_BS, 4096, 2048, 7168)
+            cfg.c_store = policy
+            assert fn(p, p, p, p, p, 4096, 2048, 7168, ctypes.byref(cfg), None) == 4
 
 
 def test_offsets_past_32_bits_rejected(fb):

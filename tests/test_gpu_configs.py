@@ -28,14 +28,16 @@ def fb():
 
 
 def _configs(fb, route, N):
+    """Every tile with five tile orders; the C store policy (0, 1, 2) varies with the order, so
+    every tile runs each policy."""
     out = []
-    for (bm, bn, wm, wn, st, pp), (gm, xcd, pers) in itertools.product(
-            TILES, ((1, 0, 0), (3, 1, 1), (2, 0, 1), (2, 2, 1), (1, 2, 0))):
+    for (bm, bn, wm, wn, st, pp), (gm, xcd, pers, cst) in itertools.product(
+            TILES, ((1, 0, 0, 0), (3, 1, 1, 2), (2, 0, 1, 1), (2, 2, 1, 2), (1, 2, 0, 1))):
         tm, tn = bm // wm, bn // wn
         ok = (tn <= 128 and 128 % tn == 0) if route == fb.ROUTE_BS else \
             (tm % 64 == 0 and tn % 64 == 0 and st * (bm + bn) * 132 <= 160 * 1024)
         if ok and N % bn == 0:
-            out.append(fb.Config(bm, bn, wm, wn, st, gm, xcd, pers, pp))
+            out.append(fb.Config(bm, bn, wm, wn, st, gm, xcd, pers, pp, 0, cst))
     return out
 
 
@@ -98,7 +100,9 @@ def test_invalid_configs_rejected(fb):
                 fb.Config(256, 128, 4, 2, 3, 1, 1, 1, 1),  # ping-pong needs two stages
                 fb.Config(256, 128, 4, 2, 3, 1, 1, 1, 3),  # no such schedule
                 fb.Config(256, 128, 4, 2, 3, 1, 1, 1, 4),  # no such schedule
-                fb.Config(256, 128, 4, 2, 2, 1, 1, 1, 2)):  # warp-specialised, not with 2 stages
+                fb.Config(256, 128, 4, 2, 2, 1, 1, 1, 2),  # warp-specialised, not with 2 stages
+                fb.Config(128, 128, 2, 2, 3, 1, 1, 1, 2, 0, 3),  # no such C store policy
+                fb.Config(128, 128, 2, 2, 3, 1, 1, 1, 2, 0, -1)):
         with pytest.raises(fb.Fp8bsError) as e:
             fb.fp8bs_gemm_with_config(A, sa, Bp, sb, C, cfg)
         assert e.value.status == 4

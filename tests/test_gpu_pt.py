@@ -73,11 +73,12 @@ def test_pt_all_configs_bitwise_equal(fb, oracle, M, N, K):
     _, ref = oracle.pt_gemm(z.A, z.a_scale, z.B, z.b_scale)
     parity(ref_bits, ref, f"pt default {M}x{N}x{K}")
     n = 0
-    for (bm, bn, wm, wn, st, pp), (gm, xcd, pers) in itertools.product(TILES, ((1, 0, 0), (3, 1, 1), (2, 2, 1))):
+    for (bm, bn, wm, wn, st, pp), (gm, xcd, pers, cst) in itertools.product(
+            TILES, ((1, 0, 0, 1), (3, 1, 1, 0), (2, 2, 1, 2))):
         if N % bn:
             continue
-        got = run_pt(fb, z, fb.Config(bm, bn, wm, wn, st, gm, xcd, pers, pp))
-        assert np.array_equal(got, ref_bits), f"{(bm, bn, wm, wn, st, pp, gm, xcd, pers)}: differs"
+        got = run_pt(fb, z, fb.Config(bm, bn, wm, wn, st, gm, xcd, pers, pp, 0, cst))
+        assert np.array_equal(got, ref_bits), f"{(bm, bn, wm, wn, st, pp, gm, xcd, pers, cst)}: differs"
         n += 1
     assert n >= 20
 

@@ -647,8 +647,9 @@ SWEEP_TILES = [(256, 256, 2, 4, 2, 0), (256, 128, 4, 2, 3, 2), (128, 256, 2, 4, 
 
 def tile_sweep_mode(name: str, stream, group_ms=(2, 4, 8, 16), tiles=None) -> int:
     """Every tile order (group_m x XCD mapping) for each tile in `tiles` on one workload, through
-    the *_with_config entry. The library's own choice is checked against the oracle first; every
-    other configuration must give the same bits (all do the same per-element arithmetic)."""
+    the *_with_config entry, with the selected C store policy; then the three store policies on
+    the selected tile and order. The library's own choice is checked against the oracle first;
+    every other configuration must give the same bits (all do the same per-element arithmetic)."""
     import torch
 
     import fp8_block_scaled_e4m3_amd as fb
@@ -661,25 +662,30 @@ def tile_sweep_mode(name: str, stream, group_ms=(2, 4, 8, 16), tiles=None) -> in
     rows = [dict(config="selected", **case.config, us=round(min(base_med) * 1e6, 2))]
     log(f"[tile-sweep] {name} selected {rows[-1]} parity {par}")
     fn = {"bs": fb.fp8bs_gemm_with_config, "mx": fb.fp8mx_gemm_with_config, "pt": fb.fp8pt_gemm_with_config}[case.route]
-    for (bm, bn, wm, wn, st, pp) in (tiles or SWEEP_TILES):
-        if case.N % bn:
+    sel = case.config
+    cst = sel.get("c_store", 0)
+    cand = [(t, gm, xcd, cst) for t in (tiles or SWEEP_TILES) for gm in group_ms for xcd in (0, 1, 2)]
+    cand += [((sel["block_m"], sel["block_n"], sel["waves_m"], sel["waves_n"], sel["stages"], sel["pingpong"]),
+              sel["group_m"], sel["xcd_remap"], c) for c in (0, 1, 2)]
+    skip = set()
+    for (bm, bn, wm, wn, st, pp), gm, xcd, c in cand:
+        if case.N % bn or (bm, bn, wm, wn, st, pp) in skip:
             continue
-        for gm in group_ms:
-            for xcd in (0, 1, 2):
-                cfg = fb.Config(bm, bn, wm, wn, st, gm, xcd, 1, pp)
-                case.launch = lambda cfg=cfg: fn(case.A, case.sa, case.B, case.sb, case.C, cfg, stream)
-                case.C.fill_(0)
-                try:
-                    case.fast_launch(stream, cfg)
-                except fb.Fp8bsError as e:  # not instantiated for this route
-                    log(f"[tile-sweep] {cfg}: {e}")
-                    break
-                torch.cuda.synchronize()
-                same = bool(torch.equal(case.C, ref))
-                med, _ = case.repeated(stream, preroll_ms=30.0, time_s=0.02)
-                rows.append(dict(tile=f"{bm}x{bn}", waves=f"{wm}x{wn}", stages=st, pingpong=pp, group_m=gm,
-                                 xcd_remap=xcd, us=round(min(med) * 1e6, 2), bitwise_equal=same))
-                log(f"[tile-sweep] {rows[-1]}")
+        cfg = fb.Config(bm, bn, wm, wn, st, gm, xcd, 1, pp, 0, c)
+        case.launch = lambda cfg=cfg: fn(case.A, case.sa, case.B, case.sb, case.C, cfg, stream)
+        case.C.fill_(0)
+        try:
+            case.fast_launch(stream, cfg)
+        except fb.Fp8bsError as e:  # not instantiated for this route
+            log(f"[tile-sweep] {cfg}: {e}")
+            skip.add((bm, bn, wm, wn, st, pp))
+            continue
+        torch.cuda.synchronize()
+        same = bool(torch.equal(case.C, ref))
+        med, _ = case.repeated(stream, preroll_ms=30.0, time_s=0.02)
+        rows.append(dict(tile=f"{bm}x{bn}", waves=f"{wm}x{wn}", stages=st, pingpong=pp, group_m=gm,
+                         xcd_remap=xcd, c_store=c, us=round(min(med) * 1e6, 2), bitwise_equal=same))
+        log(f"[tile-sweep] {rows[-1]}")
     print(json.dumps({"mode": "tile_sweep", "workload": name, "parity": par, "rows": rows}), flush=True)
     return 0
 
@@ -877,12 +883,15 @@ def sweep_md(path: str) -> int:
                 "every other configuration gave the same bits (bitwise_equal). Times: minimum over 3 runs of the",
                 "median per-launch time.", "",
                 f"Selected: {sel['block_m']}x{sel['block_n']} waves {sel['waves_m']}x{sel['waves_n']}, {sel['stages']} "
-                f"stages, schedule {sel['pingpong']}, group_m {sel['group_m']}, XCD mapping {sel['xcd_remap']}: "
-                f"**{sel['us']} us**.", "",
-                "| tile | waves | stages | schedule | group_m | XCD mapping | us | same bits |", "|---|---|---|---|---|---|---|---|"]
+                f"stages, schedule {sel['pingpong']}, group_m {sel['group_m']}, XCD mapping {sel['xcd_remap']}, "
+                f"C store policy {sel.get('c_store', 0)}: **{sel['us']} us**. The tile orders run with the selected "
+                "store policy; the selected tile and order also with each of the three policies (0 write-back, "
+                "1 written through the L2, 2 written through and non-temporal).", "",
+                "| tile | waves | stages | schedule | group_m | XCD mapping | C store | us | same bits |",
+                "|---|---|---|---|---|---|---|---|---|"]
         for r in sorted(rows[1:], key=lambda r: r["us"]):
             out.append(f"| {r['tile']} | {r['waves']} | {r['stages']} | {r['pingpong']} | {r['group_m']} | "
-                       f"{r['xcd_remap']} | {r['us']} | {r['bitwise_equal']} |")
+                       f"{r['xcd_remap']} | {r.get('c_store', 0)} | {r['us']} | {r['bitwise_equal']} |")
     print("\n".join(out))
     return 0
 

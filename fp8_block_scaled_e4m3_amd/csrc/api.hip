@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kVersion = 10100;  // 1.1.0
+constexpr int kVersion = 10200;  // 1.2.0: fp8bs_config.c_store
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
@@ -110,27 +110,27 @@ fp8bs_config select(int route, int M, int N, int K)
     // weight panel is reused by the tile rows that need it while it is still cached (measured
     // on the 4096 x 65536 x 1536 shape: about 12% faster than mapping 1, 5% faster than
     // round-robin; on the 16384 x 8192 x 1280 shape mapping 1 is 6% faster than mapping 2).
-    // C store policy (all three give the same bits; measured per shape, each policy forced
-    // through the *_with_config entry, alternating, on three boxes):
-    //  * C larger than the 256 MiB memory-side cache: written through as non-temporal lines
-    //    (2), which keeps C from pushing the operands out of that cache (4096 x 65536 x 1536:
-    //    392.8 against 403.3 us; written through without the hint, 423 against 413).
-    //  * At most three rounds of tiles: written through the L2 (1). A few rounds' stores come
-    //    close to the kernel's end, and lines still dirty in the L2s then are written back
+    // C store policy by the size of C (all three give the same bits; each policy forced through
+    // the *_with_config entry, alternating, on several boxes):
+    //  * larger than the 256 MiB memory-side cache: written through as non-temporal lines (2),
+    //    which keeps C from pushing the operands out of that cache (4096 x 65536 x 1536:
+    //    392.8 against 403.3 us; written through without the hint, 423 against 413; 16384 x
+    //    16384 x 1536 on 128 x 256 tiles: 399 against 514);
+    //  * at most 64 MiB: written through the L2 (1). Such a C is written in few rounds of tiles,
+    //    close to the kernel's end, and what is still dirty in the L2s then is written back
     //    after the last tile (4096 x 2048 x 7168: 51.0 against 52.5 us, the route-PT twin 43.8
-    //    against 45.5; 4096 x 8192 x 1536, two rounds: 50.2 against 51.9; 16384 x 1536 x 7168,
-    //    three rounds: 148.5 against 149.4).
-    //  * Otherwise the ordinary write-back stores: with more rounds the L2 absorbs each round's
-    //    burst (16384 x 5120 x 2048, five rounds: 137.6 against 138.5 written through, 140.5
-    //    non-temporal; 16384 x 7168 x 768, seven rounds: from 3% faster to 5% slower written
-    //    through depending on the box, 4-7% slower non-temporal).
-    auto cfg = [&](int variant, int block_n) {
-        const int xcd = group_m * (N / block_n) <= 2 * kCUs ? 1 : 2;
-        const int block_m = fp8bs::variant_info(variant)->block_m;
-        const int c_store = (int64_t)M * N * 2 > ((int64_t)256 << 20) ? 2
-                            : tiles(block_m, block_n) <= 3 * kCUs     ? 1
-                                                                      : 0;
-        return make_config(variant, group_m, xcd, 1, c_store);
+    //    against 45.5; 4096 x 8192 x 1536: 50.2 against 51.9, on 128 x 256 tiles 51.2 against
+    //    53.5; 16384 x 1536 x 7168: 148.5 against 149.4);
+    //  * in between, the ordinary write-back stores, which the L2 absorbs round by round
+    //    (16384 x 5120 x 2048: 137.6 against 138.5 written through, 140.5 non-temporal;
+    //    16384 x 7168 x 768: from 3% faster to 5% slower written through depending on the box,
+    //    on 128 x 256 tiles 109.4 against 103.1; 8192 x 8192 x 2048 and 4096 x 16384 x 7168 on
+    //    128 x 256 tiles: 127.7 against 127.6, 416.9 against 406.2).
+    const int64_t c_bytes = (int64_t)M * N * 2;
+    const int c_store = c_bytes > ((int64_t)256 << 20) ? 2 : c_bytes <= ((int64_t)64 << 20) ? 1 : 0;
+    auto cfg = [&](int variant, int block_n, int gm = group_m) {
+        const int xcd = gm * (N / block_n) <= 2 * kCUs ? 1 : 2;
+        return make_config(variant, gm, xcd, 1, c_store);
     };
     // The small-M kernel against the main kernel. With few rows the main kernel runs one round
     // of 128-row tiles whose time is set by the K loop (warp-specialised 128 x 128 tiles, route
@@ -187,8 +187,19 @@ fp8bs_config select(int route, int M, int N, int K)
     // 24576 x 1536, M = 1024: 384 tiles in two rounds, 51.4 against 42.5 for 768 of 256 x 128
     // in three; 36864 x 7168, M = 1024: 576 tiles in three rounds, 286.7 against 258.6 for 1152
     // in five)
+    // Route BS at K <= 1536 takes the warp-specialised 128 x 256 tile there instead where those
+    // make at least four rounds of the CUs, walked in bands of 8 tile rows (1024 rows, as 4 rows
+    // of 256-row tiles): with few K blocks per tile and several tiles per workgroup, its loader
+    // waves keep the next tile's operands coming while the computing waves store C
+    // (16384 x 7168 x 768: 103.1 against 105.7 us; 4096 x 65536 x 1536: 408.4 against 421.1;
+    // 4096 x 8192 x 1536: 51.2 against 51.4; 16384 x 16384 x 1536: 399.2 against 393.4, whose
+    // runs spread over 393-406). Deeper K keeps the 256 x 256
+    // tile (8192 x 8192 x 2048: 127.6 against 126.4; 4096 x 16384 x 7168: 406.2 against 386.1),
+    // and so do routes MX and PT, which have no promote (route PT, 4096 x 65536 x 1536: 418.1
+    // against 396.0).
     if (N % 256 == 0 && tiles(256, 256) >= kCUs && 2 * rounds(256, 256) <= rounds(256, 128))
-        return cfg(2, 256);
+        return route == fp8bs::kRouteBS && K <= 1536 && tiles(128, 256) >= 4 * kCUs ? cfg(14, 256, 8)
+                                                                                    : cfg(2, 256);
     // the 256x128 / 128x256 tiles run warp-specialised (four loader waves beside the eight
     // math waves): measured 5-7% faster than the same tiles with every wave loading on the
     // 4096 x 2048 x 7168 and 16384 x 1536 x 7168 shapes

@@ -83,10 +83,15 @@ def test_zero_rows_is_accepted_without_pointers(fb):
 
 def test_select_config_is_shape_driven(fb):
     """The configuration depends on (M, N, K) only; large shapes take the 256x256 tile (with
-    the XCD remap unless the output is very wide), narrow grids a smaller tile that still
+    the XCD remap unless the output is very wide), except route BS at K <= 1536, which takes
+    the warp-specialised 128x256 tile in 8-row bands; narrow grids a smaller tile that still
     fills the device."""
     big = fb.fp8bs_select_config(fb.ROUTE_BS, 16384, 7168, 768)
-    assert (big.block_m, big.block_n) == (256, 256) and big.xcd_remap == 1
+    assert (big.block_m, big.block_n, big.pingpong, big.group_m, big.xcd_remap) == (128, 256, 2, 8, 1)
+    for route, shape in ((fb.ROUTE_BS, (8192, 8192, 2048)), (fb.ROUTE_BS, (4096, 16384, 7168)),
+                         (fb.ROUTE_PT, (16384, 7168, 768)), (fb.ROUTE_MX, (16384, 8192, 1280))):
+        c = fb.fp8bs_select_config(route, *shape)
+        assert (c.block_m, c.block_n, c.pingpong, c.group_m, c.xcd_remap) == (256, 256, 0, 4, 1), (route, shape)
     nn = fb.fp8bs_select_config(fb.ROUTE_BS, 4096, 2048, 7168)
     assert ((4096 + nn.block_m - 1) // nn.block_m) * (2048 // nn.block_n) >= 256
     # narrow-N: 128x256 tiles, 8 math waves (2x4) plus the four loader waves of schedule 2
@@ -98,15 +103,18 @@ def test_select_config_is_shape_driven(fb):
     assert (nn_odd.block_m, nn_odd.block_n, nn_odd.pingpong) == (256, 128, 2)
     mx = fb.fp8bs_select_config(fb.ROUTE_MX, 4096, 192, 256)  # N % 128 != 0: the 128x64 tile
     assert (mx.small_m, mx.block_n) == (0, 64)
-    wide = fb.fp8bs_select_config(fb.ROUTE_BS, 4096, 65536, 1536)  # 1024-tile bands: round-local order
-    assert (wide.block_m, wide.block_n) == (256, 256) and wide.xcd_remap == 2
+    wide = fb.fp8bs_select_config(fb.ROUTE_BS, 4096, 65536, 1536)  # 2048-tile bands: round-local order
+    assert (wide.block_m, wide.block_n, wide.group_m) == (128, 256, 8) and wide.xcd_remap == 2
+    wide_pt = fb.fp8bs_select_config(fb.ROUTE_PT, 4096, 65536, 1536)
+    assert (wide_pt.block_m, wide_pt.block_n) == (256, 256) and wide_pt.xcd_remap == 2
     # C stores: non-temporal and written through for a C larger than 256 MiB, written through
-    # for at most three rounds of tiles, ordinary stores otherwise
+    # for a C of at most 64 MiB, ordinary stores otherwise
     assert nn.c_store == 1 and wide.c_store == 2 and big.c_store == 0 and nn16.c_store == 1
     for route, shape, policy in ((fb.ROUTE_MX, (16384, 8192, 1280), 0), (fb.ROUTE_MX, (16384, 8192 + 256, 1280), 2),
                                  (fb.ROUTE_BS, (4096, 8192, 1536), 1), (fb.ROUTE_PT, (4096, 2048, 7168), 1),
                                  (fb.ROUTE_BS, (128, 65536, 1536), 1), (fb.ROUTE_BS, (1, 128, 128), 0),
-                                 (fb.ROUTE_MX, (16384, 5120, 2048), 0)):
+                                 (fb.ROUTE_MX, (16384, 5120, 2048), 0), (fb.ROUTE_BS, (4096, 8192 + 256, 1536), 0),
+                                 (fb.ROUTE_BS, (16384, 16384, 1536), 2)):
         assert fb.fp8bs_select_config(route, *shape).c_store == policy, (route, shape)
     for route, shape in ((fb.ROUTE_BS, (4096, 65536, 1536)), (fb.ROUTE_MX, (16384, 8192, 1280)),
                          (fb.ROUTE_BS, (128, 256, 512)), (fb.ROUTE_BS, (1, 128, 128))):

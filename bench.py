@@ -582,13 +582,19 @@ def ksweep_mode(M: int, N: int, Ks, stream) -> int:
     """Time against depth at a fixed output shape, routes BS and PT (the same matrix work without
     the per-block promote), each point parity-checked before it is timed; fit
     time = fixed + slope * (K/128) per route (page "Flydsl Fp8 Blockscale Gemm", Bottleneck
-    diagnosis: the K sweep separates a shape's fixed cost from its mainloop)."""
+    diagnosis: the K sweep separates a shape's fixed cost from its mainloop). Every point of a
+    route runs the configuration the library selects at the first (shallowest) K, so that the
+    fit describes one kernel even where the selection changes with K."""
     import torch
+
+    import fp8_block_scaled_e4m3_amd as fb
     out = {"mode": "ksweep", "M": M, "N": N, "routes": {}}
     for route in ("bs", "pt"):
         pts = []
+        rid = fb.ROUTE_PT if route == "pt" else fb.ROUTE_BS
+        fixed = fb.fp8bs_select_config(rid, M, N, Ks[0])
         for K in Ks:
-            case = Case(f"ksweep_{M}x{N}", 0, stream, twin=(route == "pt"), shape=(M, N, K))
+            case = Case(f"ksweep_{M}x{N}", 0, stream, twin=(route == "pt"), shape=(M, N, K), config=fixed)
             case.launch()
             torch.cuda.synchronize()
             par = sampled_parity(case, 8, 8)
@@ -846,7 +852,8 @@ def sweep_md(path: str) -> int:
                 "Command (R = repository root):", "", "```",
                 f"python3 R/bench.py --ksweep --ksweep-shape {d['M']},{d['N']} --ksweep-k {ks} > OUT/ksweep.json",
                 "python3 R/bench.py --sweep-md OUT/ksweep.json", "```", "",
-                "Each point: the library's own configuration for the shape, parity against the oracle on 8 sampled",
+                "Each point: the configuration the library selects at the shallowest K (per route, below), through",
+                "the *_with_config entry, parity against the oracle on 8 sampled",
                 "rows and 8 sampled columns checked before timing, then the minimum over 3 runs of the median",
                 "per-launch time (5 groups of back-to-back launches per run, HIP events on the stream).",
                 "Least-squares fit: time = fixed + slope x (K / 128).", "",
@@ -858,8 +865,8 @@ def sweep_md(path: str) -> int:
         out += ["", "| route | fixed us | us per K block | max residual us |", "|---|---|---|---|"]
         for r, v in d["routes"].items():
             out.append(f"| {r} | {v['fixed_us']} | {v['us_per_k_block']} | {v['max_residual_us']} |")
-        cfg = d["routes"]["bs"]["points"][0]["config"]
-        out += ["", f"Configuration (both routes): {cfg}."]
+        for r, v in d["routes"].items():
+            out += ["", f"Configuration ({r}): {v['points'][0]['config']}."]
     elif d["mode"] == "loop_probe":
         out += [f"# Loop skeleton on the {d['workload']} operand bytes", "",
                 "Command (R = repository root):", "", "```",

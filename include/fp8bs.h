@@ -61,7 +61,8 @@ typedef enum {
     FP8BS_E_WORKSPACE = 6 /* a workspace is missing, misaligned or too small             */
 } fp8bs_status;
 
-/* Version of this ABI (major * 10000 + minor * 100 + patch). */
+/* Version of this ABI (major * 10000 + minor * 100 + patch). 1.2.0 added the c_store field
+ * at the end of fp8bs_config (the struct grew by 4 bytes). */
 int fp8bs_version(void);
 
 /* Static, human-readable text for a status code (never NULL). */

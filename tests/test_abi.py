@@ -38,7 +38,8 @@ def test_every_declared_symbol_is_exported(fb):
 
 
 def test_version_and_strerror(fb):
-    assert fb.fp8bs_version() >= 10000
+    assert fb.fp8bs_version() >= 10200  # fp8bs_config with c_store
+    assert ctypes.sizeof(fb.Config) == 11 * 4
     for code in range(6):
         assert fb.fp8bs_strerror(code)
     assert fb.fp8bs_strerror(99) == "unknown status"

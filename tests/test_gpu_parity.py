@@ -44,6 +44,20 @@ def test_mx_small_full(fb, oracle, M, N, K, seed):
     parity(got, ref, f"mx {M}x{N}x{K} seed {seed}")
 
 
+# ragged M through the plain entry on shapes where the selector takes paths the workloads do
+# not: 8200 x 7168 x 768 the warp-specialised 128x256 tile in 8-row bands with loader priority
+# (route BS, K <= 1536), its last tile row 8 rows deep; 2000 x 8192 x 1536 the 256x256 tile with
+# C written through the L2; 4100 x 4352 x 7168 the 128x256 tile at deep K, C written through;
+# 8195 x 16896 x 256 a C over 256 MiB, written through as non-temporal lines
+@pytest.mark.parametrize("M,N,K", [(8200, 7168, 768), (2000, 8192, 1536), (4100, 4352, 7168), (8195, 16896, 256)])
+def test_bs_selector_paths_ragged_full(fb, oracle, M, N, K):
+    c = fb.fp8bs_select_config(fb.ROUTE_BS, M, N, K)
+    x = workload.bs_inputs(M, N, K, 3)
+    got = run_bs(fb, x)
+    _, ref = oracle.bs_gemm(x.A, x.a_scale, x.B, x.b_scale)
+    parity(got, ref, f"bs {M}x{N}x{K} ({c})")
+
+
 @pytest.mark.parametrize("seed", [0, 1, 2, 3])
 def test_tiny_workload_full_every_seed(fb, oracle, seed):
     """The tiny workload (128 x 256 x 512) in full for seeds 0-3, through the plain entry point
